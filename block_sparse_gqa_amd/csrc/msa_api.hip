@@ -1,0 +1,170 @@
+// C ABI of the MSA hot path (declared in include/msa.h): argument
+// validation, workspace sizing and kernel dispatch.  Nothing here allocates,
+// frees or synchronises; every check runs on the host before any launch.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "../../include/msa.h"
+#include "msa_internal.h"
+
+using msa::Shape;
+
+namespace {
+
+bool supported_common(const msa_problem_t &p) {
+    return (p.block_size == 64 || p.block_size == 128) && p.top_k >= 1 && p.top_k <= 4096;
+}
+
+// Structural validity shared by every op.  Returns MSA_SUCCESS or an error.
+msa_status_t check_problem(const msa_problem_t *p) {
+    if (p == nullptr) return MSA_ERROR_INVALID_VALUE;
+    if (p->num_seqs < 1 || p->total_q < 0 || p->total_k < 0) return MSA_ERROR_INVALID_VALUE;
+    if (p->cu_seqlens_q == nullptr || p->cu_seqlens_k == nullptr) return MSA_ERROR_INVALID_VALUE;
+    if (p->num_heads < 1 || p->num_kv_heads < 1 || p->num_heads % p->num_kv_heads != 0)
+        return MSA_ERROR_INVALID_VALUE;
+    if (p->head_dim < 1 || p->index_dim < 1 || p->block_size < 1 || p->top_k < 1) return MSA_ERROR_INVALID_VALUE;
+    if (p->total_q > 0 && (p->max_seqlen_q < 1 || p->max_seqlen_k < p->max_seqlen_q || p->total_k < 1))
+        return MSA_ERROR_INVALID_VALUE;
+    if (p->max_seqlen_q > p->total_q || p->max_seqlen_k > p->total_k) return MSA_ERROR_INVALID_VALUE;
+    if (!supported_common(*p)) return MSA_ERROR_NOT_SUPPORTED;
+    return MSA_SUCCESS;
+}
+
+Shape to_shape(const msa_problem_t &p) {
+    Shape s;
+    s.num_seqs = p.num_seqs;
+    s.total_q = p.total_q;
+    s.total_k = p.total_k;
+    s.max_q = p.max_seqlen_q;
+    s.max_k = p.max_seqlen_k;
+    s.H = p.num_heads;
+    s.h = p.num_kv_heads;
+    s.d = p.head_dim;
+    s.d_idx = p.index_dim;
+    s.B = p.block_size;
+    s.top_k = p.top_k;
+    s.cu_q = p.cu_seqlens_q;
+    s.cu_k = p.cu_seqlens_k;
+    return s;
+}
+
+msa_status_t index_support(const msa_problem_t &p) {
+    if (p.index_dim != 32 && p.index_dim != 64) return MSA_ERROR_NOT_SUPPORTED;
+    if (p.num_kv_heads > 64) return MSA_ERROR_NOT_SUPPORTED;
+    if (p.max_seqlen_q == 1 && p.num_kv_heads > 16) return MSA_ERROR_NOT_SUPPORTED;
+    const long e = ((long)p.max_seqlen_k + p.block_size - 1) / p.block_size;
+    if (e > msa::max_select_blocks()) return MSA_ERROR_NOT_SUPPORTED;
+    return MSA_SUCCESS;
+}
+
+msa_status_t attn_support(const msa_problem_t &p) {
+    if (p.head_dim != 64 && p.head_dim != 128) return MSA_ERROR_NOT_SUPPORTED;
+    if (p.num_heads / p.num_kv_heads > 16) return MSA_ERROR_NOT_SUPPORTED;
+    return MSA_SUCCESS;
+}
+
+size_t index_ws(const msa_problem_t &p) {
+    Shape s = to_shape(p);
+    return (size_t)p.total_q * p.num_kv_heads * (size_t)msa::score_stride(s) * sizeof(float);
+}
+
+msa_status_t check_ws(void *ws, size_t have, size_t need) {
+    if (need == 0) return MSA_SUCCESS;
+    if (ws == nullptr || have < need) return MSA_ERROR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return MSA_ERROR_WORKSPACE;
+    return MSA_SUCCESS;
+}
+
+msa_status_t launched(hipError_t e) { return e == hipSuccess ? MSA_SUCCESS : MSA_ERROR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *msa_status_string(msa_status_t status) {
+    switch (status) {
+        case MSA_SUCCESS: return "success";
+        case MSA_ERROR_INVALID_VALUE: return "invalid value";
+        case MSA_ERROR_NOT_SUPPORTED: return "shape not supported";
+        case MSA_ERROR_WORKSPACE: return "workspace missing or too small";
+        case MSA_ERROR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+size_t msa_workspace_size(int op, const msa_problem_t *problem) {
+    if (check_problem(problem) != MSA_SUCCESS) return (size_t)-1;
+    const msa_problem_t &p = *problem;
+    switch (op) {
+        case MSA_OP_INDEX_TOPK:
+            if (index_support(p) != MSA_SUCCESS) return (size_t)-1;
+            return index_ws(p);
+        case MSA_OP_SPARSE_ATTN_PREFILL:
+            if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
+            return 0;
+        case MSA_OP_SPARSE_ATTN_DECODE:
+            if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
+            if (p.max_seqlen_q != 1 || p.total_q != p.num_seqs) return (size_t)-1;
+            return msa::decode_workspace_bytes(to_shape(p));
+    }
+    return (size_t)-1;
+}
+
+msa_status_t msa_index_topk(const msa_problem_t *problem, const msa_bf16_t *q_idx, const msa_bf16_t *k_idx,
+                            int32_t *topk_ids, void *workspace, size_t workspace_bytes, msa_stream_t stream) {
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if (q_idx == nullptr || k_idx == nullptr || topk_ids == nullptr) return MSA_ERROR_INVALID_VALUE;
+    if ((st = index_support(p)) != MSA_SUCCESS) return st;
+    if ((st = check_ws(workspace, workspace_bytes, index_ws(p))) != MSA_SUCCESS) return st;
+    Shape s = to_shape(p);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    float *scores = reinterpret_cast<float *>(workspace);
+    hipError_t e = (p.max_seqlen_q == 1) ? msa::launch_index_decode(s, q_idx, k_idx, scores, hs)
+                                         : msa::launch_index_prefill(s, q_idx, k_idx, scores, hs);
+    if (e != hipSuccess) return MSA_ERROR_LAUNCH;
+    return launched(msa::launch_topk_select(s, scores, topk_ids, hs));
+}
+
+msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
+                                     const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
+                                     msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
+                                     msa_stream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if (q == nullptr || k == nullptr || v == nullptr || topk_ids == nullptr || out == nullptr)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
+    if ((st = attn_support(p)) != MSA_SUCCESS) return st;
+    Shape s = to_shape(p);
+    return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k_cache,
+                                    const msa_bf16_t *v_cache, const int32_t *topk_ids, float softmax_scale,
+                                    msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
+                                    msa_stream_t stream) {
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if (p.max_seqlen_q != 1 || p.total_q != p.num_seqs) return MSA_ERROR_INVALID_VALUE;
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || topk_ids == nullptr || out == nullptr)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
+    if ((st = attn_support(p)) != MSA_SUCCESS) return st;
+    Shape s = to_shape(p);
+    if ((st = check_ws(workspace, workspace_bytes, msa::decode_workspace_bytes(s))) != MSA_SUCCESS) return st;
+    return launched(msa::launch_attn_decode(s, q, k_cache, v_cache, topk_ids, softmax_scale, out, lse, workspace,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device-side helpers for the gfx950 MSA kernels: bf16 packing, MFMA wrappers,
+// cross-lane reductions and the monotone float key used for selection.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// 16-byte global load that yields zeros when `ok` is false (no memory access then).
+__device__ __forceinline__ uint4 load16_if(const void *p, bool ok) {
+    uint4 z = {0u, 0u, 0u, 0u};
+    return ok ? *reinterpret_cast<const uint4 *>(p) : z;
+}
+
+// D(16x16, f32) += A(16x32) * B(32x16).  Operand layout (lane l, q = l / 16):
+//   A: row l % 16, k = 8q .. 8q+7;  B: column l % 16, k = 8q .. 8q+7;
+//   D: column l % 16, rows 4q .. 4q+3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32, f32) += A(32x16) * B(16x32).  Operand layout (lane l, q = l / 32):
+//   A: row l % 32, k = 8q .. 8q+7;  B: column l % 32, k = 8q .. 8q+7;
+//   D[i] (i < 16): column l % 32, row 8*(i/4) + 4q + (i%4).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Reductions with the lane 16 (resp. 32) positions away: the swap returns the
+// own value in one slot and the partner's in the other.
+__device__ __forceinline__ float max_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte chunks addressed by the group's
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4, in that order.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void *lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)((__attribute__((address_space(3))) char *)lds_ptr));
+}
+
+// Order-preserving map of a float32 onto uint32 (larger float -> larger key).
+// -0.0 is folded onto +0.0 so both zeros tie.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Completes this wave's outstanding LDS operations; also a compiler barrier.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+}  // namespace msa

@@ -1,0 +1,40 @@
+// Host-side launch helpers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct Shape {
+    int num_seqs, total_q, total_k, max_q, max_k;
+    int H, h, d, d_idx, B, top_k;
+    const int32_t *cu_q, *cu_k;
+};
+
+// Block-level scores workspace: [total_q, h, e_stride] float32.
+inline int score_stride(const Shape &s) {
+    int e = (s.max_k + s.B - 1) / s.B;
+    return (e + 3) / 4 * 4;
+}
+
+// Index branch, step 1+2: token scores (never stored) max-pooled per block.
+hipError_t launch_index_prefill(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx,
+                                float *scores, hipStream_t st);
+hipError_t launch_index_decode(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx,
+                               float *scores, hipStream_t st);
+// Index branch, step 3: per (row, group) top-k of the block scores.
+hipError_t launch_topk_select(const Shape &s, const float *scores, int32_t *ids, hipStream_t st);
+int max_select_blocks();
+
+// Sparse branch.
+hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st);
+int decode_splits(const Shape &s);
+size_t decode_workspace_bytes(const Shape &s);
+hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
+                              hipStream_t st);
+
+}  // namespace msa

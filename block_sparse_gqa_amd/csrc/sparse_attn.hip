@@ -1,0 +1,380 @@
+// Sparse branch: exact softmax attention of the G query heads of one GQA
+// group over the blocks that group selected, read from the original,
+// uncompressed K/V ("MiniMax M3 MSA vs Step 3.7 Flash MFA", section "MSA: a
+// minimal sparse attention", second layer: the heads of a group share one
+// selection, so one load of a K/V block serves all G heads; "MiniMax Goes
+// Sparse", section 1, step 2).
+//
+// One wave owns one (query, group).  The G heads sit on the N side of
+// v_mfma_f32_16x16x32_bf16 (padded to 16).  Per 64-token sub-block:
+//   S^T = K . Q^T   A = K rows straight from HBM (16 tokens x 16 bytes per
+//                   lane, coalesced), B = Q^T held in registers;
+//   online softmax in the exp2 domain, per head = per lane column;
+//   O^T += V^T . P^T  B = P^T comes from the S^T accumulators without any data
+//                   movement (the contraction index is permuted consistently on
+//                   both sides), A = V^T is read from a token-major LDS copy
+//                   of the V block with the transposing ds_read_b64_tr_b16.
+// Decode splits a sequence's selected blocks over many waves and merges the
+// partial results by log-sum-exp; prefill gives every (query, group) its own
+// wave.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kSub = 64;   // tokens per sub-block
+
+template <int D>
+struct VTile {
+    static constexpr int ROWB = D * 2 + 16;   // padded row bytes in LDS
+    static constexpr int BYTES = kSub * ROWB;
+};
+
+template <int D>
+struct Acc {
+    f32x4 o[D / 16];   // O^T: lane l -> head l%16, dims dt*16 + 4*(l/16) + i
+    float m;           // running max (log2 domain), same in the 4 lanes of a head
+    float l;           // this lane's partial sum of exp2
+};
+
+// Attend one 64-token sub-block starting at sequence-local token t0.
+// Tokens t > p (causal) or t >= len_k are masked.
+template <int D>
+__device__ __forceinline__ void attend_sub(Acc<D> &acc, const bf16x8 (&qop)[D / 32], const uint16_t *__restrict__ k,
+                                           const uint16_t *__restrict__ v, size_t k_begin, int len_k, int p, int t0,
+                                           int h, int g, float c2, char *vlds) {
+    constexpr int KS = D / 32;
+    constexpr int DT = D / 16;
+    constexpr int CPR = D / 8;                         // 16-byte chunks per V row
+    constexpr int VLOADS = kSub * CPR / 64;
+    const int lane = lane_id();
+    const int q4 = lane >> 4, l16 = lane & 15;
+
+    // V sub-block -> registers (zeros beyond the sequence) -> LDS, token-major.
+    uint4 vr[VLOADS];
+#pragma unroll
+    for (int x = 0; x < VLOADS; ++x) {
+        const int ci = x * 64 + lane;
+        const int tok = ci / CPR, c16 = ci % CPR;
+        const int t = t0 + tok;
+        vr[x] = load16_if(v + ((k_begin + t) * h + g) * D + c16 * 8, t < len_k);
+    }
+    // K operands (A of S^T = K . Q^T): token t0 + tt*16 + l16, dims 32*ks + 8*q4.
+    uint4 kr[4][KS];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = t0 + tt * 16 + l16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kr[tt][ks] = load16_if(k + ((k_begin + t) * h + g) * D + 32 * ks + 8 * q4, t < len_k);
+    }
+#pragma unroll
+    for (int x = 0; x < VLOADS; ++x) {
+        const int ci = x * 64 + lane;
+        const int tok = ci / CPR, c16 = ci % CPR;
+        *reinterpret_cast<uint4 *>(vlds + tok * VTile<D>::ROWB + c16 * 16) = vr[x];
+    }
+
+    f32x4 s[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[tt] = mfma16x16x32(as_bf16x8(kr[tt][ks]), qop[ks], s[tt]);
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + tt * 16 + 4 * q4 + i;
+            float x = s[tt][i] * c2;
+            x = (t <= p && t < len_k) ? x : -INFINITY;
+            s[tt][i] = x;
+            mloc = fmaxf(mloc, x);
+        }
+    mloc = max_xor16(mloc);
+    mloc = max_xor32(mloc);
+    const float m_new = fmaxf(acc.m, mloc);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = exp2f(acc.m - m_use);
+    acc.m = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e = exp2f(s[tt][i] - m_use);
+            s[tt][i] = e;
+            lsum += e;
+        }
+    acc.l = acc.l * alpha + lsum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc.o[dt] *= alpha;
+
+    wave_lds_sync();   // V tile visible to the whole wave
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        // B = P^T: slots 8*q4 + i <- token 32*s2 + 4*q4 + i, slots 8*q4 + 4 + i <- token 32*s2 + 16 + 4*q4 + i.
+        // P is split into a bf16 head and a bf16 tail (p = hi + lo + O(2^-17 p)), so the
+        // probabilities keep float32-like accuracy even when only a few tokens are visible.
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = s[2 * s2][i];
+            pv[4 + i] = s[2 * s2 + 1][i];
+        }
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t h0 = f32_to_bf16_rne(pv[2 * i]), h1 = f32_to_bf16_rne(pv[2 * i + 1]);
+            hi[i] = h0 | (h1 << 16);
+            lo[i] = pack_bf16x2(pv[2 * i] - __uint_as_float(h0 << 16), pv[2 * i + 1] - __uint_as_float(h1 << 16));
+        }
+        const bf16x8 pop_hi = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
+        const bf16x8 pop_lo = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
+        const int tok_a = 32 * s2 + 4 * q4 + (l16 >> 2);
+        const int tok_b = tok_a + 16;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int col = dt * 16 + 4 * (l16 & 3);
+            const i16x4 va = lds_read_tr16(vlds + tok_a * VTile<D>::ROWB + col * 2);
+            const i16x4 vb = lds_read_tr16(vlds + tok_b * VTile<D>::ROWB + col * 2);
+            uint4 au;
+            au.x = (uint32_t)(uint16_t)va[0] | ((uint32_t)(uint16_t)va[1] << 16);
+            au.y = (uint32_t)(uint16_t)va[2] | ((uint32_t)(uint16_t)va[3] << 16);
+            au.z = (uint32_t)(uint16_t)vb[0] | ((uint32_t)(uint16_t)vb[1] << 16);
+            au.w = (uint32_t)(uint16_t)vb[2] | ((uint32_t)(uint16_t)vb[3] << 16);
+            acc.o[dt] = mfma16x16x32(as_bf16x8(au), pop_hi, acc.o[dt]);
+            acc.o[dt] = mfma16x16x32(as_bf16x8(au), pop_lo, acc.o[dt]);
+        }
+    }
+    wave_lds_sync();   // reads of the V tile done before the next sub-block overwrites it
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qop)[D / 32], const uint16_t *q, size_t row, int H, int head0, int G) {
+    const int lane = lane_id();
+    const int hq = lane & 15, q4 = lane >> 4;
+    const bool ok = hq < G;
+    const uint16_t *src = q + (row * H + head0 + hq) * D + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qop[ks] = as_bf16x8(load16_if(src + 32 * ks, ok));
+}
+
+template <int D>
+__device__ __forceinline__ void init_acc(Acc<D> &acc) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.m = -INFINITY;
+    acc.l = 0.0f;
+}
+
+// Sum the 4 per-lane partials of each head.
+__device__ __forceinline__ float head_total(float l) {
+    l = sum_xor16(l);
+    return sum_xor32(l);
+}
+
+__device__ __forceinline__ int find_seq(const int32_t *cu_q, int num_seqs, int row) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------- prefill
+template <int D, int B>
+__global__ __launch_bounds__(64) void attn_prefill_wave(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
+    int num_seqs, int H, int h, int top_k, float c2, uint16_t *__restrict__ out, float *__restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) char vlds[VTile<D>::BYTES];
+    const int row = blockIdx.x;
+    const int g = blockIdx.y;
+    const int G = H / h;
+    const int s = find_seq(cu_q, num_seqs, row);
+    const int len_q = cu_q[s + 1] - cu_q[s];
+    const size_t k_begin = (size_t)cu_k[s];
+    const int len_k = cu_k[s + 1] - cu_k[s];
+    const int p = len_k - len_q + (row - cu_q[s]);
+
+    bf16x8 qop[D / 32];
+    load_q<D>(qop, q, (size_t)row, H, g * G, G);
+    Acc<D> acc;
+    init_acc<D>(acc);
+    const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
+    for (int a = 0; a < top_k; ++a) {
+        const int j = sel[a];
+        if (j < 0 || j > p / B) continue;   // unused slot (or an id outside the causal range)
+#pragma unroll
+        for (int sb = 0; sb < B / kSub; ++sb) {
+            const int t0 = j * B + sb * kSub;
+            if (t0 > p) break;
+            attend_sub<D>(acc, qop, k, v, k_begin, len_k, p, t0, h, g, c2, vlds);
+        }
+    }
+    const float l = head_total(acc.l);
+    const int lane = lane_id();
+    const int hq = lane & 15, q4 = lane >> 4;
+    if (hq < G) {
+        const float inv = l > 0.f ? 1.0f / l : 0.0f;
+        uint16_t *o = out + ((size_t)row * H + g * G + hq) * D + 4 * q4;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            uint2 w;
+            w.x = pack_bf16x2(acc.o[dt][0] * inv, acc.o[dt][1] * inv);
+            w.y = pack_bf16x2(acc.o[dt][2] * inv, acc.o[dt][3] * inv);
+            *reinterpret_cast<uint2 *>(o + dt * 16) = w;
+        }
+        if (lse != nullptr && q4 == 0)
+            lse[(size_t)row * H + g * G + hq] = l > 0.f ? (acc.m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------- decode
+template <int D, int B>
+__global__ __launch_bounds__(64) void attn_decode_split(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
+    int H, int h, int top_k, int per_split, float c2, float *__restrict__ part_o, float *__restrict__ part_lse) {
+    __shared__ __attribute__((aligned(16))) char vlds[VTile<D>::BYTES];
+    const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+    const int nsplit = gridDim.x;
+    const int G = H / h;
+    const int row = cu_q[s + 1] - 1;
+    const size_t k_begin = (size_t)cu_k[s];
+    const int len_k = cu_k[s + 1] - cu_k[s];
+    const int p = len_k - 1;
+
+    bf16x8 qop[D / 32];
+    load_q<D>(qop, q, (size_t)row, H, g * G, G);
+    Acc<D> acc;
+    init_acc<D>(acc);
+    const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
+    const int a0 = split * per_split, a1 = min(top_k, a0 + per_split);
+    for (int a = a0; a < a1; ++a) {
+        const int j = sel[a];
+        if (j < 0 || j > p / B) continue;   // unused slot (or an id outside the causal range)
+#pragma unroll
+        for (int sb = 0; sb < B / kSub; ++sb) {
+            const int t0 = j * B + sb * kSub;
+            if (t0 > p) break;
+            attend_sub<D>(acc, qop, k, v, k_begin, len_k, p, t0, h, g, c2, vlds);
+        }
+    }
+    const float l = head_total(acc.l);
+    const int lane = lane_id();
+    const int hq = lane & 15, q4 = lane >> 4;
+    if (hq < G) {
+        const size_t slot = (((size_t)s * H + g * G + hq) * nsplit + split);
+        const float inv = l > 0.f ? 1.0f / l : 0.0f;
+        float *o = part_o + slot * D + 4 * q4;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            *reinterpret_cast<float4 *>(o + dt * 16) =
+                make_float4(acc.o[dt][0] * inv, acc.o[dt][1] * inv, acc.o[dt][2] * inv, acc.o[dt][3] * inv);
+        if (q4 == 0) part_lse[slot] = l > 0.f ? acc.m + log2f(l) : -INFINITY;   // log2 domain
+    }
+}
+
+// One wave per (sequence, head): O = sum_s w_s O_s / sum_s w_s, w_s = 2^(lse_s - max).
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_merge(const float *__restrict__ part_o,
+                                                        const float *__restrict__ part_lse, int H, int nsplit,
+                                                        uint16_t *__restrict__ out, float *__restrict__ lse) {
+    const int head = blockIdx.x, s = blockIdx.y;
+    const int lane = lane_id();
+    const size_t base = ((size_t)s * H + head) * nsplit;
+    float m = -INFINITY;
+    for (int x = lane; x < nsplit; x += 64) m = fmaxf(m, part_lse[base + x]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    constexpr int PER = D / 64;
+    float o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    float wsum = 0.f;
+    for (int x = 0; x < nsplit; ++x) {
+        const float ls = part_lse[base + x];
+        if (ls == -INFINITY) continue;
+        const float w = exp2f(ls - m);
+        wsum += w;
+        const float *src = part_o + (base + x) * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += w * src[lane * PER + i];
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    uint16_t *dst = out + ((size_t)s * H + head) * D + lane * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) dst[i] = (uint16_t)f32_to_bf16_rne(o[i] * inv);
+    if (lse != nullptr && lane == 0)
+        lse[(size_t)s * H + head] = wsum > 0.f ? (m + log2f(wsum)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <int D, int B>
+hipError_t launch_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
+    dim3 grid(s.total_q, s.h);
+    hipLaunchKernelGGL((attn_prefill_wave<D, B>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.num_seqs,
+                       s.H, s.h, s.top_k, scale * kLog2e, out, lse);
+    return hipGetLastError();
+}
+
+template <int D, int B>
+hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws, hipStream_t st) {
+    const int nsplit = decode_splits(s);
+    const int per = (s.top_k + nsplit - 1) / nsplit;
+    float *part_o = reinterpret_cast<float *>(ws);
+    float *part_lse = part_o + (size_t)s.num_seqs * s.H * nsplit * s.d;
+    hipLaunchKernelGGL((attn_decode_split<D, B>), dim3(nsplit, s.h, s.num_seqs), dim3(64), 0, st, q, k, v, ids,
+                       s.cu_q, s.cu_k, s.H, s.h, s.top_k, per, scale * kLog2e, part_o, part_lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_decode_merge<D>), dim3(s.H, s.num_seqs), dim3(64), 0, st, part_o, part_lse, s.H, nsplit,
+                       out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_splits(const Shape &s) {
+    // Aim for ~2048 waves in flight; each split keeps at least one block.
+    long pairs = (long)s.num_seqs * s.h;
+    long want = (2048 + pairs - 1) / pairs;
+    if (want > s.top_k) want = s.top_k;
+    if (want < 1) want = 1;
+    if (want > 256) want = 256;
+    return (int)want;
+}
+
+size_t decode_workspace_bytes(const Shape &s) {
+    const size_t n = (size_t)s.num_seqs * s.H * decode_splits(s);
+    return n * (size_t)s.d * sizeof(float) + n * sizeof(float);
+}
+
+hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
+    if (s.d == 64 && s.B == 64) return launch_prefill<64, 64>(s, q, k, v, ids, scale, out, lse, st);
+    if (s.d == 64 && s.B == 128) return launch_prefill<64, 128>(s, q, k, v, ids, scale, out, lse, st);
+    if (s.d == 128 && s.B == 64) return launch_prefill<128, 64>(s, q, k, v, ids, scale, out, lse, st);
+    if (s.d == 128 && s.B == 128) return launch_prefill<128, 128>(s, q, k, v, ids, scale, out, lse, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
+                              hipStream_t st) {
+    if (s.d == 64 && s.B == 64) return launch_decode<64, 64>(s, q, k, v, ids, scale, out, lse, ws, st);
+    if (s.d == 64 && s.B == 128) return launch_decode<64, 128>(s, q, k, v, ids, scale, out, lse, ws, st);
+    if (s.d == 128 && s.B == 64) return launch_decode<128, 64>(s, q, k, v, ids, scale, out, lse, ws, st);
+    if (s.d == 128 && s.B == 128) return launch_decode<128, 128>(s, q, k, v, ids, scale, out, lse, ws, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace msa

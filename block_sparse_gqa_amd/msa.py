@@ -1,0 +1,159 @@
+"""Thin ctypes binding of libmsa.so (include/msa.h).
+
+Argument marshalling only: every step of the MSA hot path runs in the HIP
+kernels behind the C ABI.  Tensors are torch tensors on the GPU (PyTorch is
+used for device memory and streams); each call enqueues on the given stream
+(default: torch's current stream) and raises MsaError on a non-zero status.
+The library must have been built (``python -m block_sparse_gqa_amd.build``);
+loading fails loudly otherwise -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_SUCCESS = 0
+MSA_ERROR_INVALID_VALUE = 1
+MSA_ERROR_NOT_SUPPORTED = 2
+MSA_ERROR_WORKSPACE = 3
+MSA_ERROR_LAUNCH = 4
+
+MSA_OP_INDEX_TOPK = 0
+MSA_OP_SPARSE_ATTN_PREFILL = 1
+MSA_OP_SPARSE_ATTN_DECODE = 2
+
+SIZE_MAX = (1 << 64) - 1
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class msa_problem_t(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_k", ctypes.c_void_p),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load libmsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_gqa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    prob = ctypes.POINTER(msa_problem_t)
+    lib.msa_index_topk.argtypes = [prob, P, P, P, P, S, P]
+    lib.msa_index_topk.restype = ctypes.c_int
+    lib.msa_sparse_attn_prefill.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
+    lib.msa_sparse_attn_prefill.restype = ctypes.c_int
+    lib.msa_sparse_attn_decode.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
+    lib.msa_sparse_attn_decode.restype = ctypes.c_int
+    lib.msa_workspace_size.argtypes = [ctypes.c_int, prob]
+    lib.msa_workspace_size.restype = S
+    lib.msa_status_string.argtypes = [ctypes.c_int]
+    lib.msa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().msa_status_string(int(status)).decode()
+
+
+def _ptr(x):
+    """Device address of a torch tensor, or an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_problem(cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads,
+                 num_kv_heads, head_dim, index_dim, block_size, top_k) -> msa_problem_t:
+    """cu_seqlens_* are device int32 tensors (or addresses); the rest are host ints."""
+    p = msa_problem_t()
+    p.num_seqs = _nseq(cu_seqlens_q)
+    p.total_q, p.total_k = int(total_q), int(total_k)
+    p.cu_seqlens_q, p.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    p.max_seqlen_q, p.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    p.num_heads, p.num_kv_heads = int(num_heads), int(num_kv_heads)
+    p.head_dim, p.index_dim = int(head_dim), int(index_dim)
+    p.block_size, p.top_k = int(block_size), int(top_k)
+    return p
+
+
+def _nseq(cu):
+    if isinstance(cu, int):
+        raise ValueError("pass cu_seqlens as a tensor so num_seqs is known")
+    return int(cu.numel()) - 1
+
+
+def msa_workspace_size(op: int, problem: msa_problem_t) -> int:
+    n = load().msa_workspace_size(int(op), ctypes.byref(problem))
+    if n == SIZE_MAX:
+        raise MsaError(MSA_ERROR_NOT_SUPPORTED, "msa_workspace_size")
+    return int(n)
+
+
+def _check(status, what):
+    if status != MSA_SUCCESS:
+        raise MsaError(status, what)
+
+
+def _nbytes(ws):
+    if ws is None:
+        return 0
+    return ws.numel() * ws.element_size()
+
+
+def msa_index_topk(problem, q_idx, k_idx, topk_ids, workspace=None, stream=None):
+    _check(load().msa_index_topk(ctypes.byref(problem), _ptr(q_idx), _ptr(k_idx), _ptr(topk_ids),
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream)), "msa_index_topk")
+
+
+def msa_sparse_attn_prefill(problem, q, k, v, topk_ids, softmax_scale, out, lse=None, workspace=None,
+                            stream=None):
+    _check(load().msa_sparse_attn_prefill(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_ids),
+                                          float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                          _nbytes(workspace), _stream(stream)), "msa_sparse_attn_prefill")
+
+
+def msa_sparse_attn_decode(problem, q, k_cache, v_cache, topk_ids, softmax_scale, out, lse=None, workspace=None,
+                           stream=None):
+    _check(load().msa_sparse_attn_decode(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(topk_ids), float(softmax_scale), _ptr(out), _ptr(lse),
+                                         _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "msa_sparse_attn_decode")

@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every symbol include/msa.h declares, and
+rejects bad arguments on the host before touching the GPU.  No compute call
+runs here: every call below fails validation, so nothing is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_gqa_amd import msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+FAKE = 0x1000   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(msa.LIB_PATH):
+        from block_sparse_gqa_amd import build
+        build.build()
+    return msa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"msa_index_topk", "msa_sparse_attn_prefill", "msa_sparse_attn_decode",
+                          "msa_workspace_size", "msa_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert msa.status_string(code)
+    assert msa.status_string(99) == "unknown status"
+
+
+def prob(**kw):
+    p = msa.msa_problem_t()
+    base = dict(num_seqs=1, total_q=128, total_k=128, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=128,
+                max_seqlen_k=128, num_heads=8, num_kv_heads=2, head_dim=128, index_dim=64, block_size=64, top_k=4)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def index_call(lib, p, q_idx=FAKE, k_idx=FAKE, ids=FAKE, ws=None, ws_bytes=0):
+    return lib.msa_index_topk(ctypes.byref(p) if p is not None else None, q_idx, k_idx, ids, ws, ws_bytes, None)
+
+
+def test_workspace_size(lib):
+    p = prob()
+    # [total_q, h, round_up(ceil(max_k / B), 4)] float32 block scores
+    assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p)) == 128 * 2 * 4 * 4
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == 0
+    # decode needs max_seqlen_q == 1
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_DECODE, ctypes.byref(p)) == msa.SIZE_MAX
+    d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)
+    assert 0 < lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_DECODE, ctypes.byref(d)) < msa.SIZE_MAX
+    assert lib.msa_workspace_size(7, ctypes.byref(p)) == msa.SIZE_MAX
+    assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(prob(index_dim=48))) == msa.SIZE_MAX
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=6, num_kv_heads=4), msa.MSA_ERROR_INVALID_VALUE),
+    (dict(num_seqs=0), msa.MSA_ERROR_INVALID_VALUE),
+    (dict(top_k=0), msa.MSA_ERROR_INVALID_VALUE),
+    (dict(cu_seqlens_q=None), msa.MSA_ERROR_INVALID_VALUE),
+    (dict(max_seqlen_q=256), msa.MSA_ERROR_INVALID_VALUE),
+    (dict(max_seqlen_k=64), msa.MSA_ERROR_INVALID_VALUE),
+    (dict(block_size=32), msa.MSA_ERROR_NOT_SUPPORTED),
+    (dict(index_dim=48), msa.MSA_ERROR_NOT_SUPPORTED),
+    (dict(top_k=5000), msa.MSA_ERROR_NOT_SUPPORTED),
+    (dict(num_kv_heads=128, num_heads=128), msa.MSA_ERROR_NOT_SUPPORTED),
+])
+def test_index_topk_rejects(lib, kw, status):
+    assert index_call(lib, prob(**kw)) == status
+
+
+def test_index_topk_null_and_workspace(lib):
+    assert index_call(lib, None) == msa.MSA_ERROR_INVALID_VALUE
+    assert index_call(lib, prob(), q_idx=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert index_call(lib, prob(), ids=None) == msa.MSA_ERROR_INVALID_VALUE
+    need = 128 * 2 * 4 * 4
+    assert index_call(lib, prob(), ws=None, ws_bytes=0) == msa.MSA_ERROR_WORKSPACE
+    assert index_call(lib, prob(), ws=FAKE, ws_bytes=need - 1) == msa.MSA_ERROR_WORKSPACE
+    assert index_call(lib, prob(), ws=FAKE + 4, ws_bytes=need) == msa.MSA_ERROR_WORKSPACE   # misaligned
+    # empty input: nothing to do, success without touching anything
+    assert index_call(lib, prob(total_q=0, max_seqlen_q=0), q_idx=None, ids=None) == msa.MSA_SUCCESS
+
+
+def attn_call(lib, fn, p, q=FAKE, out=FAKE, scale=0.088, ws=None, ws_bytes=0):
+    return fn(ctypes.byref(p), q, FAKE, FAKE, FAKE, ctypes.c_float(scale), out, None, ws, ws_bytes, None)
+
+
+def test_attention_rejects(lib):
+    pre, dec = lib.msa_sparse_attn_prefill, lib.msa_sparse_attn_decode
+    assert attn_call(lib, pre, prob(head_dim=96)) == msa.MSA_ERROR_NOT_SUPPORTED
+    assert attn_call(lib, pre, prob(num_heads=34, num_kv_heads=2)) == msa.MSA_ERROR_NOT_SUPPORTED   # G = 17
+    assert attn_call(lib, pre, prob(), q=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert attn_call(lib, pre, prob(), out=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert attn_call(lib, pre, prob(), scale=0.0) == msa.MSA_ERROR_INVALID_VALUE
+    assert attn_call(lib, pre, prob(), scale=float("nan")) == msa.MSA_ERROR_INVALID_VALUE
+    # decode demands one query per sequence
+    assert attn_call(lib, dec, prob()) == msa.MSA_ERROR_INVALID_VALUE
+    d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)
+    assert attn_call(lib, dec, d, ws=None) == msa.MSA_ERROR_WORKSPACE
