@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X.
+
+One step = one pass of the whole hot path over the two headline workloads:
+  * decode at 1M context: 4 sequences x 1 query, H=64, h=8, d=128, d_idx=64,
+    B=64, k=1024  (msa_index_topk + msa_sparse_attn_decode)
+  * causal prefill of 32768 tokens: H=32, h=8, d=128, d_idx=64, B=64, k=32,
+    clustered keys  (msa_index_topk + msa_sparse_attn_prefill)
+Inputs are seeded synthetic bf16 tensors, resident in HBM before timing starts.
+
+Prints one JSON line: whole-step tokens/s, per-workload results, the roofline
+of the dominant kernel (algorithmic bytes or flops per launch over its HIP-event
+duration) and the CPU oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MSA tokens/s: decode@1M ctx & prefill@32k; % of HBM/MFMA roofline"
+WORKLOADS = ("decode_1m", "prefill_32k")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_tokens(ids, cu_q, cu_k, B):
+    """Per (row, group): number of visible tokens in the selected blocks (torch, on device)."""
+    import torch
+    total_q, h, k = ids.shape
+    rows = torch.arange(total_q, device=ids.device)
+    seq = torch.searchsorted(cu_q.long(), rows, right=True) - 1
+    len_q = (cu_q[1:] - cu_q[:-1]).long()[seq]
+    len_k = (cu_k[1:] - cu_k[:-1]).long()[seq]
+    p = (len_k - len_q + rows - cu_q.long()[seq]).view(total_q, 1, 1)
+    j = ids.long()
+    n = torch.clamp(p - j * B + 1, min=0, max=B)
+    return torch.where(j >= 0, n, torch.zeros_like(n)).sum(dim=2)   # [total_q, h]
+
+
+def algorithmic(inp, dp, ids):
+    """Algorithmic work of each entry point (what MSA itself must move or compute)."""
+    wl = inp.wl
+    H, h, d, di, B = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.index_dim, wl.block_size
+    vis = visible_tokens(ids, dp.cu_q, dp.cu_k, B)            # [total_q, h]
+    tok_sel = int(vis.sum().item())
+    lens_q = np.diff(inp.cu_seqlens_q).astype(np.int64)
+    lens_k = np.diff(inp.cu_seqlens_k).astype(np.int64)
+    # index scores: every query scores every visible key for each group
+    sum_vis_keys = int(sum(((lk - lq) * lq + lq * (lq + 1) // 2) for lq, lk in zip(lens_q, lens_k)))
+    index_flops = 2.0 * di * h * sum_vis_keys
+    attn_flops = 4.0 * d * (H // h) * tok_sel
+    index_bytes = float(wl.total_k * di * 2 + wl.total_q * h * di * 2 + wl.total_q * h * wl.top_k * 4)
+    attn_bytes = float(tok_sel * d * 2 * 2 + 2 * wl.total_q * H * d * 2 + wl.total_q * h * wl.top_k * 4)
+    return dict(index_flops=index_flops, attn_flops=attn_flops, index_bytes=index_bytes, attn_bytes=attn_bytes,
+                selected_tokens=tok_sel)
+
+
+def cpu_baseline(inputs, sample_rows=192, seed=7):
+    """The oracle (untuned) on a bounded sample of the step, scaled to tokens/s."""
+    import oracle
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    parts, secs = [], 0.0
+    for name, inp in inputs.items():
+        wl = inp.wl
+        if wl.is_decode:
+            rows = np.array([0], dtype=np.int64)         # one of the sequences
+            scale = wl.total_q / 1.0
+            desc = f"{name}: 1 of {wl.total_q} sequences"
+        else:
+            rng = np.random.Generator(np.random.PCG64(seed))
+            rows = np.sort(rng.choice(wl.total_q, size=min(sample_rows, wl.total_q), replace=False))
+            scale = wl.total_q / len(rows)
+            desc = f"{name}: {len(rows)} uniformly drawn rows of {wl.total_q}"
+        t0 = time.perf_counter()
+        ids, _, _ = oracle.index_topk(inp, rows, threads=threads)
+        oracle.sparse_attention(inp, ids, rows, threads=threads)
+        dt = time.perf_counter() - t0
+        secs += dt * scale
+        parts.append(f"{desc} ({dt:.1f} s)")
+    tokens = sum(inp.wl.total_q for inp in inputs.values())
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(parts) + "; extrapolated linearly to the full step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workloads", default=",".join(WORKLOADS))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding of this path is "
+              "described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_sparse_gqa_amd import device, msa, synth
+    msa.load()
+    torch.cuda.set_device(0)
+    names = [n for n in args.workloads.split(",") if n]
+
+    inputs, dps, bufs = {}, {}, {}
+    for name in names:
+        log(f"[bench] generating {name}")
+        inp = synth.make_inputs(name)
+        inputs[name] = inp
+        dps[name] = device.upload(inp)
+        ids = device.alloc_ids(dps[name])
+        out, lse = device.alloc_out(dps[name])
+        bufs[name] = (ids, out, lse)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, name in enumerate(names):
+            dp = dps[name]
+            ids, out, lse = bufs[name]
+            if events is not None:
+                events[name][0].record()
+            device.index_topk(dp, ids)
+            if events is not None:
+                events[name][1].record()
+            device.sparse_attention(dp, ids, out, lse)
+            if events is not None:
+                events[name][2].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)] for n in names}
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step({n: ev[n][s] for n in names})
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    results, kernels = {}, []
+    total_tokens = 0
+    for name in names:
+        inp, dp = inputs[name], dps[name]
+        ids = bufs[name][0]
+        t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[name]]))
+        t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in ev[name]]))
+        alg = algorithmic(inp, dp, ids)
+        wl = inp.wl
+        total_tokens += wl.total_q
+        r = {"tokens": wl.total_q, "ms": t_idx + t_att, "tokens_per_s": wl.total_q / ((t_idx + t_att) * 1e-3),
+             "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "selected_tokens": alg["selected_tokens"],
+             "workload": wl.description}
+        if wl.is_decode:
+            gbs_i = alg["index_bytes"] / (t_idx * 1e-3) / 1e9
+            gbs_a = alg["attn_bytes"] / (t_att * 1e-3) / 1e9
+            tot = (alg["index_bytes"] + alg["attn_bytes"]) / ((t_idx + t_att) * 1e-3) / 1e9
+            r.update({"bound": "hbm", "algorithmic_GB": (alg["index_bytes"] + alg["attn_bytes"]) / 1e9,
+                      "GB_per_s": tot, "frac_hbm_peak": tot / HBM_PEAK_GBS,
+                      "index_topk_GB_per_s": gbs_i, "sparse_attn_GB_per_s": gbs_a})
+            kernels.append(("msa_index_topk[%s]" % name, t_idx, "hbm", alg["index_bytes"]))
+            kernels.append(("msa_sparse_attn_decode[%s]" % name, t_att, "hbm", alg["attn_bytes"]))
+        else:
+            tf_i = alg["index_flops"] / (t_idx * 1e-3) / 1e12
+            tf_a = alg["attn_flops"] / (t_att * 1e-3) / 1e12
+            tot = (alg["index_flops"] + alg["attn_flops"]) / ((t_idx + t_att) * 1e-3) / 1e12
+            r.update({"bound": "mfma", "algorithmic_TFLOP": (alg["index_flops"] + alg["attn_flops"]) / 1e12,
+                      "TFLOP_per_s": tot, "frac_mfma_peak": tot / MFMA_BF16_PEAK_TFLOPS,
+                      "index_topk_TFLOP_per_s": tf_i, "sparse_attn_TFLOP_per_s": tf_a})
+            kernels.append(("msa_index_topk[%s]" % name, t_idx, "mfma", alg["index_flops"]))
+            kernels.append(("msa_sparse_attn_prefill[%s]" % name, t_att, "mfma", alg["attn_flops"]))
+        results[name] = r
+
+    kname, kms, kbound, kwork = max(kernels, key=lambda x: x[1])
+    if kbound == "hbm":
+        achieved, peak, unit = kwork / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = kwork / (kms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    roofline = {"bound": kbound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": None, "avg_launch_ms": kms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(inputs)
+
+    line = {
+        "metric": METRIC,
+        "value": total_tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) / clustered-block bf16 inputs, generated on the host)",
+        "config": {"workload": " + ".join(names), "parallelism": "single GPU",
+                   **{n: results[n]["workload"] for n in names}},
+        "results": results,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
