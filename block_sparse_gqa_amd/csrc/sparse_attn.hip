@@ -1,4 +1,4 @@
-// Sparse branch: exact softmax attention of the G query heads of one GQA
+// Sparse branch, decode: exact softmax attention of the G query heads of one GQA
 // group over the blocks that group selected, read from the original,
 // uncompressed K/V ("MiniMax M3 MSA vs Step 3.7 Flash MFA", section "MSA: a
 // minimal sparse attention", second layer: the heads of a group share one
@@ -15,8 +15,7 @@
 //                   both sides), A = V^T is read from a token-major LDS copy
 //                   of the V block with the transposing ds_read_b64_tr_b16.
 // Decode splits a sequence's selected blocks over many waves and merges the
-// partial results by log-sum-exp; prefill gives every (query, group) its own
-// wave.
+// partial results by log-sum-exp.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -178,63 +177,6 @@ __device__ __forceinline__ float head_total(float l) {
     return sum_xor32(l);
 }
 
-__device__ __forceinline__ int find_seq(const int32_t *cu_q, int num_seqs, int row) {
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-// ---------------------------------------------------------------- prefill
-template <int D, int B>
-__global__ __launch_bounds__(64) void attn_prefill_wave(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
-    int num_seqs, int H, int h, int top_k, float c2, uint16_t *__restrict__ out, float *__restrict__ lse) {
-    __shared__ __attribute__((aligned(16))) char vlds[VTile<D>::BYTES];
-    const int row = blockIdx.x;
-    const int g = blockIdx.y;
-    const int G = H / h;
-    const int s = find_seq(cu_q, num_seqs, row);
-    const int len_q = cu_q[s + 1] - cu_q[s];
-    const size_t k_begin = (size_t)cu_k[s];
-    const int len_k = cu_k[s + 1] - cu_k[s];
-    const int p = len_k - len_q + (row - cu_q[s]);
-
-    bf16x8 qop[D / 32];
-    load_q<D>(qop, q, (size_t)row, H, g * G, G);
-    Acc<D> acc;
-    init_acc<D>(acc);
-    const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
-    for (int a = 0; a < top_k; ++a) {
-        const int j = sel[a];
-        if (j < 0 || j > p / B) continue;   // unused slot (or an id outside the causal range)
-#pragma unroll
-        for (int sb = 0; sb < B / kSub; ++sb) {
-            const int t0 = j * B + sb * kSub;
-            if (t0 > p) break;
-            attend_sub<D>(acc, qop, k, v, k_begin, len_k, p, t0, h, g, c2, vlds);
-        }
-    }
-    const float l = head_total(acc.l);
-    const int lane = lane_id();
-    const int hq = lane & 15, q4 = lane >> 4;
-    if (hq < G) {
-        const float inv = l > 0.f ? 1.0f / l : 0.0f;
-        uint16_t *o = out + ((size_t)row * H + g * G + hq) * D + 4 * q4;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            uint2 w;
-            w.x = pack_bf16x2(acc.o[dt][0] * inv, acc.o[dt][1] * inv);
-            w.y = pack_bf16x2(acc.o[dt][2] * inv, acc.o[dt][3] * inv);
-            *reinterpret_cast<uint2 *>(o + dt * 16) = w;
-        }
-        if (lse != nullptr && q4 == 0)
-            lse[(size_t)row * H + g * G + hq] = l > 0.f ? (acc.m + log2f(l)) * 0.69314718055994531f : -INFINITY;
-    }
-}
 
 // ---------------------------------------------------------------- decode
 template <int D, int B>
@@ -317,15 +259,6 @@ __global__ __launch_bounds__(64) void attn_decode_merge(const float *__restrict_
 }
 
 template <int D, int B>
-hipError_t launch_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                          const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
-    dim3 grid(s.total_q, s.h);
-    hipLaunchKernelGGL((attn_prefill_wave<D, B>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.num_seqs,
-                       s.H, s.h, s.top_k, scale * kLog2e, out, lse);
-    return hipGetLastError();
-}
-
-template <int D, int B>
 hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws, hipStream_t st) {
     const int nsplit = decode_splits(s);
@@ -356,15 +289,6 @@ int decode_splits(const Shape &s) {
 size_t decode_workspace_bytes(const Shape &s) {
     const size_t n = (size_t)s.num_seqs * s.H * decode_splits(s);
     return n * (size_t)s.d * sizeof(float) + n * sizeof(float);
-}
-
-hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                               const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
-    if (s.d == 64 && s.B == 64) return launch_prefill<64, 64>(s, q, k, v, ids, scale, out, lse, st);
-    if (s.d == 64 && s.B == 128) return launch_prefill<64, 128>(s, q, k, v, ids, scale, out, lse, st);
-    if (s.d == 128 && s.B == 64) return launch_prefill<128, 64>(s, q, k, v, ids, scale, out, lse, st);
-    if (s.d == 128 && s.B == 128) return launch_prefill<128, 128>(s, q, k, v, ids, scale, out, lse, st);
-    return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
