@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
         qbit[rt] = qidx;
         const uint16_t *src = q + ((size_t)(q_begin + r0 + qidx) * H + g * G + head) * D + 8 * q4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = as_bf16x8(load16_if(src + 32 * ks, ok));
+        for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = as_bf16x8(load16_if(src + 32 * ks, ok, q));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[rt] = -INFINITY;
@@ -108,8 +108,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
             const int tok = ci / CPR, c16 = ci % CPR;
             const int t = t0 + tok;
             const bool ok = t < len_k;
-            kst[c] = load16_if(k + ((k_begin + t) * h + g) * D + c16 * 8, ok);
-            vst[c] = load16_if(v + ((k_begin + t) * h + g) * D + c16 * 8, ok);
+            kst[c] = load16_if(k + ((k_begin + t) * h + g) * D + c16 * 8, ok, k);
+            vst[c] = load16_if(v + ((k_begin + t) * h + g) * D + c16 * 8, ok, v);
         }
     };
     auto lstore = [&](int buf) {

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     bf16x8 qop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qop[ks] = as_bf16x8(load16_if(q_idx + ((size_t)row * h + g) * DI + 32 * ks + 8 * q4, g < h));
+        qop[ks] = as_bf16x8(load16_if(q_idx + ((size_t)row * h + g) * DI + 32 * ks + 8 * q4, g < h, q_idx));
 
     for (int j = j_begin + wave; j < j_end; j += 4) {
         uint4 a[TT][KS];
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
             const int t = j * B + tt * 16 + g;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                a[tt][ks] = load16_if(k_idx + (size_t)(k_begin + t) * DI + 32 * ks + 8 * q4, t < len_k);
+                a[tt][ks] = load16_if(k_idx + (size_t)(k_begin + t) * DI + 32 * ks + 8 * q4, t < len_k, k_idx);
         }
         float m = -INFINITY;
 #pragma unroll

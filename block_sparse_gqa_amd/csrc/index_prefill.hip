@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void index_prefill_blockmax(
         col_p[nt] = ok ? shift + r : -1;
         const uint16_t *src = q_idx + ((size_t)(q_begin + r) * h + g) * DI + 8 * (lane >> 5);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = as_bf16x8(load16_if(src + 16 * ks, ok));
+        for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = as_bf16x8(load16_if(src + 16 * ks, ok, q_idx));
     }
 
     uint4 pre[PASSES];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void index_prefill_blockmax(
             const int ci = ps * 256 + tid;
             const int row = ci / CPR, c8 = ci % CPR;
             const int t = j * B + row;
-            pre[ps] = load16_if(k_idx + (size_t)(k_begin + t) * DI + c8 * 8, ci < CHUNKS && t < len_k);
+            pre[ps] = load16_if(k_idx + (size_t)(k_begin + t) * DI + c8 * 8, ci < CHUNKS && t < len_k, k_idx);
         }
     };
     auto lstore = [&](int buf) {

@@ -31,10 +31,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-// 16-byte global load that yields zeros when `ok` is false (no memory access then).
-__device__ __forceinline__ uint4 load16_if(const void *p, bool ok) {
-    uint4 z = {0u, 0u, 0u, 0u};
-    return ok ? *reinterpret_cast<const uint4 *>(p) : z;
+// 16-byte global load that yields zeros when `ok` is false.  The load itself
+// is unconditional (one global_load_dwordx4): when `ok` is false it reads the
+// always-valid address `safe` instead of `p`, and the value is then dropped.
+__device__ __forceinline__ uint4 load16_if(const void *p, bool ok, const void *safe) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(ok ? p : safe);
+    const uint4 z = {0u, 0u, 0u, 0u};
+    return ok ? v : z;
 }
 
 // D(16x16, f32) += A(16x32) * B(32x16).  Operand layout (lane l, q = l / 16):

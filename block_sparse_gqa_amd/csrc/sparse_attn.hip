@@ -58,7 +58,7 @@ __device__ __forceinline__ void attend_sub(Acc<D> &acc, const bf16x8 (&qop)[D / 
         const int ci = x * 64 + lane;
         const int tok = ci / CPR, c16 = ci % CPR;
         const int t = t0 + tok;
-        vr[x] = load16_if(v + ((k_begin + t) * h + g) * D + c16 * 8, t < len_k);
+        vr[x] = load16_if(v + ((k_begin + t) * h + g) * D + c16 * 8, t < len_k, v);
     }
     // K operands (A of S^T = K . Q^T): token t0 + tt*16 + l16, dims 32*ks + 8*q4.
     uint4 kr[4][KS];
@@ -67,7 +67,7 @@ __device__ __forceinline__ void attend_sub(Acc<D> &acc, const bf16x8 (&qop)[D / 
         const int t = t0 + tt * 16 + l16;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            kr[tt][ks] = load16_if(k + ((k_begin + t) * h + g) * D + 32 * ks + 8 * q4, t < len_k);
+            kr[tt][ks] = load16_if(k + ((k_begin + t) * h + g) * D + 32 * ks + 8 * q4, t < len_k, k);
     }
 #pragma unroll
     for (int x = 0; x < VLOADS; ++x) {
@@ -160,7 +160,7 @@ __device__ __forceinline__ void load_q(bf16x8 (&qop)[D / 32], const uint16_t *q,
     const bool ok = hq < G;
     const uint16_t *src = q + (row * H + head0 + hq) * D + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) qop[ks] = as_bf16x8(load16_if(src + 32 * ks, ok));
+    for (int ks = 0; ks < D / 32; ++ks) qop[ks] = as_bf16x8(load16_if(src + 32 * ks, ok, q));
 }
 
 template <int D>
