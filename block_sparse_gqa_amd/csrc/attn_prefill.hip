@@ -7,19 +7,29 @@
 // Reuse.  The heads of a group share one selection, and neighbouring queries
 // of a group pick overlapping block sets.  A workgroup therefore owns a tile
 // of Tq consecutive queries of one group (all G heads), forms the union of
-// their selected blocks, and streams each union block through LDS once:
-// 64-token K and V sub-blocks, double-buffered, staged by all 256 threads.
+// their selected blocks and streams each union block through LDS once, as
+// 64-token K and V sub-blocks.
 //
-// Rows.  A row is one (query, head) pair.  Each wave owns RT fixed row tiles
+// Staging.  A 4-stage LDS ring is filled with direct global->LDS loads
+// (global_load_lds_dwordx4: lane i of a load writes base + 16*i), so three
+// sub-blocks are in flight per workgroup without holding staging registers.
+// Row strides are padded (K: 2d+16 bytes, V: 2d+64 bytes) so that the K
+// operand reads and the transposing V reads are bank-conflict free; pad
+// slots are filled by the same loads and never read.  Ring reads are issued
+// in inline asm (each block waits for its own results) so the compiler does
+// not serialise them behind the in-flight ring loads; completion of a stage
+// is tracked with explicit vmcnt waits plus a barrier.
+//
+// Rows.  A row is one (query, head) pair.  Each of the NW waves owns RT fixed row tiles
 // of 16 rows (16/G queries x G heads) whose O accumulators, running max and
-// running sum stay in registers for the whole tile; for a staged block a wave
-// runs MFMA only on its row tiles that contain a query which selected the
-// block, and masks the rows whose query did not (and future tokens).
+// running sum stay in registers for the whole tile; for a staged sub-block a
+// wave runs MFMA only on its row tiles that contain a query which selected
+// the block, and masks the rows whose query did not (and future tokens).
 //   S^T = K . Q^T     v_mfma_f32_16x16x32_bf16, A = K rows from LDS,
 //                     B = Q^T resident in registers;
-//   O^T += V^T . P^T  A = V^T read from the token-major LDS copy with the
-//                     transposing ds_read_b64_tr_b16, B = P^T straight from the
-//                     S^T accumulators, split into bf16 head + tail.
+//   O^T += V^T . P^T  A = V^T read with the transposing ds_read_b64_tr_b16,
+//                     B = P^T straight from the S^T accumulators, split into
+//                     a bf16 head and tail.
 // Workgroups are numbered group-fastest, so with 8 groups all tiles of a
 // group run on the same XCD and share its L2.
 #include "msa_device.h"
@@ -29,28 +39,120 @@ namespace msa {
 
 namespace {
 
-constexpr int kWin = 256;   // key blocks per union window (one per thread)
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void gbl_void;
+
+constexpr int kWin = 256;    // key blocks per union window (one per thread)
+constexpr int kStages = 4;   // ring depth (sub-blocks)
 
 template <int D>
-struct Stage {
-    static constexpr int KROW = D * 2 + 16;   // padded LDS rows (bank-conflict free reads)
-    static constexpr int VROW = D * 2 + 32;
-    static constexpr int CH = 64 * D / 8 / 256;   // 16-byte chunks per thread per tensor
+struct Ring {
+    static constexpr int KROW = D * 2 + 16;
+    static constexpr int VROW = D * 2 + 64;
+    static constexpr int KSLOT_ROW = KROW / 16;   // 16-byte slots per row
+    static constexpr int VSLOT_ROW = VROW / 16;
+    static constexpr int KINSTR = KSLOT_ROW;      // 64 rows x slots / 64 lanes per load
+    static constexpr int VINSTR = VSLOT_ROW;
+    static constexpr int KBYTES = 64 * KROW;
+    static constexpr int VBYTES = 64 * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    // loads issued per sub-block by wave w of NW (instructions i = w, w+NW, ...)
+    template <int NW>
+    static constexpr int per_wave(int w) { return (KINSTR - w + NW - 1) / NW + (VINSTR - w + NW - 1) / NW; }
+    // waves fall into at most three classes of equal per-wave counts
+    template <int NW>
+    static constexpr int wave_class(int w) {
+        return per_wave<NW>(w) == per_wave<NW>(0) ? 0 : (per_wave<NW>(w) == per_wave<NW>(NW - 1) ? 2 : 1);
+    }
+    template <int NW>
+    static constexpr int class_rep(int c) {
+        for (int w = 0; w < NW; ++w)
+            if (wave_class<NW>(w) == c) return w;
+        return NW - 1;
+    }
 };
 
-template <int D, int RT>
-__global__ __launch_bounds__(256, 2) void attn_prefill_tile(
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// Multi-instruction asm blocks mark their outputs early-clobber ("=&v"): an
+// output register must never alias the address input that later reads in the
+// same block still use.
+
+// Four 16-byte K operand reads (k-steps 0..3, 64 bytes apart), one wait.
+__device__ __forceinline__ void lds_k4(uint4 &a0, uint4 &a1, uint4 &a2, uint4 &a3, uint32_t addr) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:64\n\t"
+        "ds_read_b128 %2, %4 offset:128\n\t"
+        "ds_read_b128 %3, %4 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+        : "v"(addr)
+        : "memory");
+}
+__device__ __forceinline__ void lds_k2(uint4 &a0, uint4 &a1, uint32_t addr) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1)
+        : "v"(addr)
+        : "memory");
+}
+
+// Transposing V reads for 4 consecutive 16-column d-tiles: for each, rows
+// tok and tok + 16 (offset ROW16 bytes), columns 32 bytes apart.
+template <int OFF, int ROW16>
+__device__ __forceinline__ void lds_v4(i16x4 (&va)[4], i16x4 (&vb)[4], uint32_t addr) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(va[0]), "=&v"(vb[0]), "=&v"(va[1]), "=&v"(vb[1]), "=&v"(va[2]), "=&v"(vb[2]), "=&v"(va[3]), "=&v"(vb[3])
+        : "v"(addr), "i"(OFF), "i"(OFF + ROW16), "i"(OFF + 32), "i"(OFF + 32 + ROW16), "i"(OFF + 64),
+          "i"(OFF + 64 + ROW16), "i"(OFF + 96), "i"(OFF + 96 + ROW16)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ unsigned long long lds_u64(uint32_t addr) {
+    unsigned long long v;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ uint4 pack_tr(i16x4 a, i16x4 b) {
+    const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+    return uint4{x.x, x.y, y.x, y.y};
+}
+
+template <int D, int RT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
     int num_seqs, int H, int h, int B, int top_k, int max_tiles, float c2, uint16_t *__restrict__ out,
     float *__restrict__ lse) {
+    using R = Ring<D>;
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
-    constexpr int CH = Stage<D>::CH;
-    constexpr int KROW = Stage<D>::KROW, VROW = Stage<D>::VROW;
-    constexpr int CPR = D / 8;
-    __shared__ __attribute__((aligned(16))) char kbuf[2][64 * KROW];
-    __shared__ __attribute__((aligned(16))) char vbuf[2][64 * VROW];
+    constexpr int CPR = D / 8;   // data slots per row
+    __shared__ __attribute__((aligned(16))) char ring[kStages * R::STAGE];
     __shared__ unsigned long long masks[kWin];
     __shared__ unsigned long long list_m[kWin];
     __shared__ int list_u[kWin];
@@ -58,7 +160,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
 
     const int G = H / h;
     const int Qt = 16 / G;                    // queries per row tile
-    const int Tq = 4 * RT * Qt;               // queries per workgroup (<= 64)
+    const int Tq = NW * RT * Qt;              // queries per workgroup (<= 64)
     const int bid = blockIdx.x;
     const int g = bid % h;
     const int rest = bid / h;
@@ -98,36 +200,93 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
         m[rt] = -INFINITY;
         l[rt] = 0.0f;
     }
-    const unsigned long long tile_bits = (Qt >= 64) ? ~0ull : ((1ull << Qt) - 1ull);
+    const unsigned long long tile_bits = (1ull << Qt) - 1ull;
 
-    uint4 kst[CH], vst[CH];
-    auto gload = [&](int t0) {
+    const uint32_t ring0 = lds_addr(ring);
+    const uint32_t list_u0 = lds_addr(list_u), list_m0 = lds_addr(list_m);
+    // Per-lane read offsets inside a stage.
+    const uint32_t k_rd = (uint32_t)(l16 * R::KROW + q4 * 16);
+    const uint32_t v_rd = (uint32_t)(R::KBYTES + (4 * q4 + (l16 >> 2)) * R::VROW + 8 * (l16 & 3));
+
+    // Direct global->LDS loads of one 64-token sub-block into a ring stage.
+    // Each lane's element offset inside a sub-block is fixed per load slot and
+    // computed once.  Pad slots read chunk 0 of their own row; for a sub-block
+    // that runs past the sequence end, rows are clamped to the last valid
+    // token (finite data, masked later), so no lane leaves the sequence.
+    constexpr int KI = (R::KINSTR + NW - 1) / NW, VI = (R::VINSTR + NW - 1) / NW;
+    uint32_t koff[KI], voff[VI];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int ci = c * 256 + tid;
-            const int tok = ci / CPR, c16 = ci % CPR;
-            const int t = t0 + tok;
-            const bool ok = t < len_k;
-            kst[c] = load16_if(k + ((k_begin + t) * h + g) * D + c16 * 8, ok, k);
-            vst[c] = load16_if(v + ((k_begin + t) * h + g) * D + c16 * 8, ok, v);
+    for (int ii = 0; ii < KI; ++ii) {
+        const int slot = (ii * NW + wave) * 64 + lane;
+        const int row = slot / R::KSLOT_ROW, c16 = slot % R::KSLOT_ROW;
+        koff[ii] = (uint32_t)(row * h * D + (c16 < CPR ? c16 : 0) * 8);
+    }
+#pragma unroll
+    for (int ii = 0; ii < VI; ++ii) {
+        const int slot = (ii * NW + wave) * 64 + lane;
+        const int row = slot / R::VSLOT_ROW, c16 = slot % R::VSLOT_ROW;
+        voff[ii] = (uint32_t)(row * h * D + (c16 < CPR ? c16 : 0) * 8);
+    }
+    auto issue = [&](int t0, int stage) {
+        char *base = ring + stage * R::STAGE;
+        const bool inside = t0 + 63 < len_k;
+        const size_t tok0 = (k_begin + t0) * h + g;
+        const uint16_t *kb = k + tok0 * D, *vb = v + tok0 * D;
+#pragma unroll
+        for (int ii = 0; ii < KI; ++ii) {
+            const int i = ii * NW + wave;
+            if (i < R::KINSTR) {
+                const uint16_t *src = kb + koff[ii];
+                if (!inside) {
+                    const int slot = i * 64 + lane;
+                    const int row = slot / R::KSLOT_ROW, c16 = slot % R::KSLOT_ROW;
+                    const int t = min(t0 + row, len_k - 1);
+                    src = k + ((k_begin + t) * h + g) * D + (c16 < CPR ? c16 : 0) * 8;
+                }
+                __builtin_amdgcn_global_load_lds((const gbl_void *)src, (lds_void *)(base + i * 1024), 16, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < VI; ++ii) {
+            const int i = ii * NW + wave;
+            if (i < R::VINSTR) {
+                const uint16_t *src = vb + voff[ii];
+                if (!inside) {
+                    const int slot = i * 64 + lane;
+                    const int row = slot / R::VSLOT_ROW, c16 = slot % R::VSLOT_ROW;
+                    const int t = min(t0 + row, len_k - 1);
+                    src = v + ((k_begin + t) * h + g) * D + (c16 < CPR ? c16 : 0) * 8;
+                }
+                __builtin_amdgcn_global_load_lds((const gbl_void *)src, (lds_void *)(base + R::KBYTES + i * 1024), 16,
+                                                 0, 0);
+            }
         }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int ci = c * 256 + tid;
-            const int tok = ci / CPR, c16 = ci % CPR;
-            *reinterpret_cast<uint4 *>(&kbuf[buf][tok * KROW + c16 * 16]) = kst[c];
-            *reinterpret_cast<uint4 *>(&vbuf[buf][tok * VROW + c16 * 16]) = vst[c];
+    // Wait until only the `ahead` sub-blocks issued after this one are still in
+    // flight (per-wave load counts differ: waves issue loads i = w, w+NW, ...).
+    auto wait_stage = [&](int ahead) {
+        const int a = ahead >= 2 ? 2 : ahead;
+        switch (R::template wave_class<NW>(wave) * 3 + a) {
+            case 0: wait_vm<0>(); break;
+            case 1: wait_vm<R::template per_wave<NW>(0)>(); break;
+            case 2: wait_vm<2 * R::template per_wave<NW>(0)>(); break;
+            case 3: wait_vm<0>(); break;
+            case 4: wait_vm<R::template per_wave<NW>(R::template class_rep<NW>(1))>(); break;
+            case 5: wait_vm<2 * R::template per_wave<NW>(R::template class_rep<NW>(1))>(); break;
+            case 6: wait_vm<0>(); break;
+            case 7: wait_vm<R::template per_wave<NW>(R::template class_rep<NW>(2))>(); break;
+            default: wait_vm<2 * R::template per_wave<NW>(R::template class_rep<NW>(2))>(); break;
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
     };
 
     for (int w0 = 0; w0 < e_tile; w0 += kWin) {
-        masks[tid] = 0ull;
+        if (tid < kWin) masks[tid] = 0ull;
         __syncthreads();
         // Which queries of the tile selected which block of this window.
         const int32_t *tile_ids = ids + ((size_t)(q_begin + r0) * h + g) * top_k;
-        for (int e = tid; e < tq_valid * top_k; e += 256) {
+        for (int e = tid; e < tq_valid * top_k; e += 64 * NW) {
             const int qi = e / top_k, a = e % top_k;
             const int j = tile_ids[(size_t)qi * h * top_k + a];
             const int pq = shift + r0 + qi;
@@ -135,15 +294,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
         }
         __syncthreads();
         // Compact the blocks somebody selected, ascending.
-        const unsigned long long mv = masks[tid];
+        const unsigned long long mv = tid < kWin ? masks[tid] : 0ull;
         const unsigned long long bal = __ballot(mv != 0ull);
         const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        if (lane == 0) wave_cnt[wave] = __builtin_popcountll(bal);
+        if (lane == 0 && wave < 4) wave_cnt[wave] = __builtin_popcountll(bal);
         __syncthreads();
         int base = 0, count = 0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            base += (w < wave) ? wave_cnt[w] : 0;
+            base += (w < wave) ? wave_cnt[w] : 0;   // waves >= 4 hold no entries
             count += wave_cnt[w];
         }
         if (mv != 0ull) {
@@ -153,19 +312,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
         __syncthreads();
 
         const int nitems = count * nsub;
-        auto t0_of = [&](int it) { return list_u[it / nsub] * B + (it % nsub) * 64; };
-        if (nitems > 0) {
-            if (t0_of(0) <= p_last) gload(t0_of(0));
-            lstore(0);
-            __syncthreads();
-        }
+        auto t0_of = [&](int it) {
+            return (int)lds_u32(list_u0 + 4 * (it / nsub)) * B + (it % nsub) * 64;
+        };
+#pragma unroll
+        for (int x = 0; x < kStages - 1; ++x)
+            if (x < nitems) issue(t0_of(x), x);
+
         for (int it = 0; it < nitems; ++it) {
-            const int buf = it & 1;
+            const int stage = it % kStages;
+            wait_stage(min(kStages - 2, nitems - 1 - it));
             const int t0 = t0_of(it);
-            const bool have_next = it + 1 < nitems;
-            const int t0n = have_next ? t0_of(it + 1) : 0;
-            if (have_next && t0n <= p_last) gload(t0n);
-            const unsigned long long mk = list_m[it / nsub];
+            const unsigned long long mk = lds_u64(list_m0 + 8 * (it / nsub));
             const unsigned long long wbits = mk >> (wave * RT * Qt);
             bool act[RT];
             bool any = false;
@@ -174,21 +332,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
                 act[rt] = ((wbits >> (rt * Qt)) & tile_bits) != 0ull;
                 any |= act[rt];
             }
+            const uint32_t sbase = ring0 + stage * R::STAGE;
             if (t0 <= p_last && any) {
                 f32x4 sacc[RT][4];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    bf16x8 a[KS];
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        a[ks] = *reinterpret_cast<const bf16x8 *>(
-                            &kbuf[buf][(tt * 16 + l16) * KROW + (32 * ks + 8 * q4) * 2]);
+                    uint4 a[KS];
+                    if constexpr (KS == 4) lds_k4(a[0], a[1], a[2], a[3], sbase + k_rd + tt * 16 * R::KROW);
+                    else lds_k2(a[0], a[1], sbase + k_rd + tt * 16 * R::KROW);
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
                         if (!act[rt]) continue;
                         sacc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) sacc[rt][tt] = mfma16x16x32(a[ks], qop[rt][ks], sacc[rt][tt]);
+                        for (int ks = 0; ks < KS; ++ks)
+                            sacc[rt][tt] = mfma16x16x32(as_bf16x8(a[ks]), qop[rt][ks], sacc[rt][tt]);
                     }
                 }
                 // online softmax per row (log2 domain)
@@ -240,39 +398,35 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
                         }
                         uint32_t hi[4], lo[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float x0 = pv[2 * i], x1 = pv[2 * i + 1];
-                            const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
-                            hi[i] = h0 | (h1 << 16);
-                            lo[i] = pack_bf16x2(x0 - __uint_as_float(h0 << 16), x1 - __uint_as_float(h1 << 16));
-                        }
+                        for (int i = 0; i < 4; ++i) hi[i] = split_bf16x2(pv[2 * i], pv[2 * i + 1], &lo[i]);
                         p_hi[rt] = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
                         p_lo[rt] = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
                     }
-                    const int tok_a = 32 * s2 + 4 * q4 + (l16 >> 2);
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const int col = dt * 16 + 4 * (l16 & 3);
-                        const i16x4 va = lds_read_tr16(&vbuf[buf][tok_a * VROW + col * 2]);
-                        const i16x4 vb = lds_read_tr16(&vbuf[buf][(tok_a + 16) * VROW + col * 2]);
-                        uint4 au;
-                        au.x = (uint32_t)(uint16_t)va[0] | ((uint32_t)(uint16_t)va[1] << 16);
-                        au.y = (uint32_t)(uint16_t)va[2] | ((uint32_t)(uint16_t)va[3] << 16);
-                        au.z = (uint32_t)(uint16_t)vb[0] | ((uint32_t)(uint16_t)vb[1] << 16);
-                        au.w = (uint32_t)(uint16_t)vb[2] | ((uint32_t)(uint16_t)vb[3] << 16);
-                        const bf16x8 vop = as_bf16x8(au);
+                    for (int dq = 0; dq < DT / 4; ++dq) {
+                        i16x4 va[4], vb[4];
+                        const uint32_t addr = sbase + v_rd + s2 * 32 * R::VROW;
+                        if (dq == 0) lds_v4<0, 16 * R::VROW>(va, vb, addr);
+                        else lds_v4<128, 16 * R::VROW>(va, vb, addr);
 #pragma unroll
-                        for (int rt = 0; rt < RT; ++rt) {
-                            if (!act[rt]) continue;
-                            o[rt][dt] = mfma16x16x32(vop, p_hi[rt], o[rt][dt]);
-                            o[rt][dt] = mfma16x16x32(vop, p_lo[rt], o[rt][dt]);
+                        for (int x = 0; x < 4; ++x) {
+                            const int dt = dq * 4 + x;
+                            const bf16x8 vop = as_bf16x8(pack_tr(va[x], vb[x]));
+#pragma unroll
+                            for (int rt = 0; rt < RT; ++rt) {
+                                if (!act[rt]) continue;
+                                o[rt][dt] = mfma16x16x32(vop, p_hi[rt], o[rt][dt]);
+                                o[rt][dt] = mfma16x16x32(vop, p_lo[rt], o[rt][dt]);
+                            }
                         }
                     }
                 }
             }
-            if (have_next) lstore(buf ^ 1);
-            __syncthreads();
+            // refill the stage read in the previous iteration (every wave is past it)
+            if (it + kStages - 1 < nitems) issue(t0_of(it + kStages - 1), (it + kStages - 1) % kStages);
         }
+        wait_vm<0>();
+        __syncthreads();
     }
 
     // Epilogue: normalise and write this wave's rows.
@@ -296,16 +450,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_tile(
     }
 }
 
-template <int D, int RT>
+template <int D, int RT, int NW>
 hipError_t launch(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *ids,
                   float scale, uint16_t *out, float *lse, hipStream_t st) {
     const int G = s.H / s.h;
-    const int Tq = 4 * RT * (16 / G);
+    const int Tq = NW * RT * (16 / G);
     const int max_tiles = (s.max_q + Tq - 1) / Tq;
     const long grid = (long)max_tiles * s.num_seqs * s.h;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_prefill_tile<D, RT>), dim3((unsigned)grid), dim3(256), 0, st, q, k, v, ids, s.cu_q,
-                       s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL((attn_prefill_tile<D, RT, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, q, k, v, ids,
+                       s.cu_q, s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, out, lse);
     return hipGetLastError();
 }
 
@@ -315,11 +469,19 @@ hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t
                                const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
     const int G = s.H / s.h;
     if (G < 1 || G > 16) return hipErrorInvalidValue;
-    const bool two = 4 * 2 * (16 / G) <= 64;   // at most 64 queries per tile (one mask bit each)
-    if (s.d == 64) return two ? launch<64, 2>(s, q, k, v, ids, scale, out, lse, st)
-                              : launch<64, 1>(s, q, k, v, ids, scale, out, lse, st);
-    if (s.d == 128) return two ? launch<128, 2>(s, q, k, v, ids, scale, out, lse, st)
-                               : launch<128, 1>(s, q, k, v, ids, scale, out, lse, st);
+    // 8 waves; two row tiles per wave when the tile stays within 64 queries
+    // (one mask bit per query), else one; 4 waves of one tile for G = 1.
+    const int qt = 16 / G;
+    if (s.d == 64) {
+        if (8 * 2 * qt <= 64) return launch<64, 2, 8>(s, q, k, v, ids, scale, out, lse, st);
+        if (8 * qt <= 64) return launch<64, 1, 8>(s, q, k, v, ids, scale, out, lse, st);
+        return launch<64, 1, 4>(s, q, k, v, ids, scale, out, lse, st);
+    }
+    if (s.d == 128) {
+        if (8 * 2 * qt <= 64) return launch<128, 2, 8>(s, q, k, v, ids, scale, out, lse, st);
+        if (8 * qt <= 64) return launch<128, 1, 8>(s, q, k, v, ids, scale, out, lse, st);
+        return launch<128, 1, 4>(s, q, k, v, ids, scale, out, lse, st);
+    }
     return hipErrorInvalidValue;
 }
 

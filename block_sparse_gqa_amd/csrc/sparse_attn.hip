@@ -127,11 +127,7 @@ __device__ __forceinline__ void attend_sub(Acc<D> &acc, const bf16x8 (&qop)[D / 
         }
         uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t h0 = f32_to_bf16_rne(pv[2 * i]), h1 = f32_to_bf16_rne(pv[2 * i + 1]);
-            hi[i] = h0 | (h1 << 16);
-            lo[i] = pack_bf16x2(pv[2 * i] - __uint_as_float(h0 << 16), pv[2 * i + 1] - __uint_as_float(h1 << 16));
-        }
+        for (int i = 0; i < 4; ++i) hi[i] = split_bf16x2(pv[2 * i], pv[2 * i + 1], &lo[i]);
         const bf16x8 pop_hi = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
         const bf16x8 pop_lo = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
         const int tok_a = 32 * s2 + 4 * q4 + (l16 >> 2);
@@ -141,11 +137,8 @@ __device__ __forceinline__ void attend_sub(Acc<D> &acc, const bf16x8 (&qop)[D / 
             const int col = dt * 16 + 4 * (l16 & 3);
             const i16x4 va = lds_read_tr16(vlds + tok_a * VTile<D>::ROWB + col * 2);
             const i16x4 vb = lds_read_tr16(vlds + tok_b * VTile<D>::ROWB + col * 2);
-            uint4 au;
-            au.x = (uint32_t)(uint16_t)va[0] | ((uint32_t)(uint16_t)va[1] << 16);
-            au.y = (uint32_t)(uint16_t)va[2] | ((uint32_t)(uint16_t)va[3] << 16);
-            au.z = (uint32_t)(uint16_t)vb[0] | ((uint32_t)(uint16_t)vb[1] << 16);
-            au.w = (uint32_t)(uint16_t)vb[2] | ((uint32_t)(uint16_t)vb[3] << 16);
+            const uint2 xa = __builtin_bit_cast(uint2, va), xb = __builtin_bit_cast(uint2, vb);
+            const uint4 au = {xa.x, xa.y, xb.x, xb.y};
             acc.o[dt] = mfma16x16x32(as_bf16x8(au), pop_hi, acc.o[dt]);
             acc.o[dt] = mfma16x16x32(as_bf16x8(au), pop_lo, acc.o[dt]);
         }
