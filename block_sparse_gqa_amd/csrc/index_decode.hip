@@ -4,11 +4,17 @@
 // single head: "MiniMax Goes Sparse", section 1, step 1; the decode scan
 // touching the full length is discussed in section 3).
 //
-// Tokens run along the MFMA M dimension of v_mfma_f32_16x16x32_bf16 and the
-// h groups along N, so each lane holds 4 tokens of one group per 16-token
+// Loads.  Each load instruction of a wave reads whole 128-byte lines (lane i
+// takes the i-th 16-byte chunk of a contiguous 1 KB run): instructions that
+// touch half lines stream markedly slower on this part.  The block is then
+// re-laid out through a padded per-wave LDS tile into the MFMA operand
+// layout.  The next block of the wave is already in flight in registers while
+// the current one is scored.
+//
+// Scores.  Tokens run along the M dimension of v_mfma_f32_16x16x32_bf16 and
+// the h groups along N, so each lane holds 4 tokens of one group per 16-token
 // tile; the Block Max Pool is an in-register max over the block's tiles plus
-// two lane swaps (xor 16, xor 32).  K_idx operands are loaded straight from
-// HBM with 16-byte loads, 16 tokens x 128 bytes per tile: fully coalesced.
+// two lane swaps (xor 16, xor 32).
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -16,13 +22,24 @@ namespace msa {
 
 namespace {
 
+constexpr int kWaves = 4;
+
+template <int DI, int B>
+struct IdxTile {
+    static constexpr int ROW = DI * 2 + 16;          // padded LDS row: conflict-free operand reads
+    static constexpr int CPR = DI / 8;               // 16-byte chunks per key row
+    static constexpr int LOADS = B * CPR / 64;       // 16-byte loads per lane per block
+};
+
 template <int DI, int B>
 __global__ __launch_bounds__(256) void index_decode_blockmax(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int h,
     float *__restrict__ scores, int e_stride, int blocks_per_wg) {
+    using T = IdxTile<DI, B>;
     constexpr int KS = DI / 32;   // 32-dim k-steps
     constexpr int TT = B / 16;    // 16-token tiles per block
+    __shared__ __attribute__((aligned(16))) char tile[kWaves][B * T::ROW];
 
     const int s = blockIdx.y;
     const int row = cu_q[s + 1] - 1;                  // the sequence's (last) query
@@ -35,36 +52,64 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, q4 = lane >> 4;
+    char *my = tile[wave];
 
     bf16x8 qop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         qop[ks] = as_bf16x8(load16_if(q_idx + ((size_t)row * h + g) * DI + 32 * ks + 8 * q4, g < h, q_idx));
 
-    for (int j = j_begin + wave; j < j_end; j += 4) {
-        uint4 a[TT][KS];
+    auto load_block = [&](uint4 (&r)[T::LOADS], int j) {
+        const int t0 = j * B;
+        const uint16_t *base = k_idx + (size_t)(k_begin + t0) * DI;
+        const bool inside = t0 + B <= len_k;
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int t = j * B + tt * 16 + g;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                a[tt][ks] = load16_if(k_idx + (size_t)(k_begin + t) * DI + 32 * ks + 8 * q4, t < len_k, k_idx);
+        for (int x = 0; x < T::LOADS; ++x) {
+            const int ci = x * 64 + lane;
+            const int tok = ci / T::CPR, c16 = ci % T::CPR;
+            if (inside) r[x] = load16(base + tok * DI + c16 * 8);
+            else r[x] = load16_if(base + tok * DI + c16 * 8, t0 + tok < len_k, k_idx);
         }
+    };
+
+    uint4 cur[T::LOADS], nxt[T::LOADS];
+    int j = j_begin + wave;
+    if (j < j_end) load_block(cur, j);
+    for (; j < j_end; j += kWaves) {
+        const bool more = j + kWaves < j_end;
+        if (more) load_block(nxt, j + kWaves);
+        // registers -> LDS (token-major, padded rows)
+#pragma unroll
+        for (int x = 0; x < T::LOADS; ++x) {
+            const int ci = x * 64 + lane;
+            const int tok = ci / T::CPR, c16 = ci % T::CPR;
+            *reinterpret_cast<uint4 *>(my + tok * T::ROW + c16 * 16) = cur[x];
+        }
+        wave_lds_sync();
         float m = -INFINITY;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(as_bf16x8(a[tt][ks]), qop[ks], acc);
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a =
+                    *reinterpret_cast<const bf16x8 *>(my + (tt * 16 + g) * T::ROW + (32 * ks + 8 * q4) * 2);
+                acc = mfma16x16x32(a, qop[ks], acc);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = j * B + tt * 16 + 4 * q4 + i;
                 m = fmaxf(m, t <= p ? acc[i] : -INFINITY);
             }
         }
+        wave_lds_sync();   // operand reads done before the next block is written
         m = max_xor16(m);
         m = max_xor32(m);
         if (lane < h) scores[((size_t)row * h + lane) * e_stride + j] = m;
+        if (more) {
+#pragma unroll
+            for (int x = 0; x < T::LOADS; ++x) cur[x] = nxt[x];
+        }
     }
 }
 

@@ -5,7 +5,7 @@
 
 #include <new>
 
-#include "../../include/msa.h"
+#include "msa.h"
 #include "msa_internal.h"
 
 using msa::Shape;

@@ -23,12 +23,18 @@ namespace msa {
 
 namespace {
 
-constexpr int kSub = 64;   // tokens per sub-block
+constexpr int kSub = 32;       // tokens per sub-block
+constexpr int kTT = kSub / 16; // 16-token MFMA tiles per sub-block
+constexpr int kChunk = 64;     // selected ids scanned per list refill
 
 template <int D>
-struct VTile {
-    static constexpr int ROWB = D * 2 + 16;   // padded row bytes in LDS
-    static constexpr int BYTES = kSub * ROWB;
+struct DecodeLds {
+    static constexpr int KROW = D * 2 + 16;   // conflict-free K operand reads
+    static constexpr int VROW = D * 2 + 32;   // conflict-free transposing V reads
+    static constexpr int KBYTES = kSub * KROW;
+    static constexpr int VBYTES = kSub * VROW;
+    static constexpr int CH = kSub * D / 8 / 64;   // 16-byte chunks per lane per tensor
+    static constexpr int KS = D / 32;
 };
 
 template <int D>
@@ -37,114 +43,6 @@ struct Acc {
     float m;           // running max (log2 domain), same in the 4 lanes of a head
     float l;           // this lane's partial sum of exp2
 };
-
-// Attend one 64-token sub-block starting at sequence-local token t0.
-// Tokens t > p (causal) or t >= len_k are masked.
-template <int D>
-__device__ __forceinline__ void attend_sub(Acc<D> &acc, const bf16x8 (&qop)[D / 32], const uint16_t *__restrict__ k,
-                                           const uint16_t *__restrict__ v, size_t k_begin, int len_k, int p, int t0,
-                                           int h, int g, float c2, char *vlds) {
-    constexpr int KS = D / 32;
-    constexpr int DT = D / 16;
-    constexpr int CPR = D / 8;                         // 16-byte chunks per V row
-    constexpr int VLOADS = kSub * CPR / 64;
-    const int lane = lane_id();
-    const int q4 = lane >> 4, l16 = lane & 15;
-
-    // V sub-block -> registers (zeros beyond the sequence) -> LDS, token-major.
-    uint4 vr[VLOADS];
-#pragma unroll
-    for (int x = 0; x < VLOADS; ++x) {
-        const int ci = x * 64 + lane;
-        const int tok = ci / CPR, c16 = ci % CPR;
-        const int t = t0 + tok;
-        vr[x] = load16_if(v + ((k_begin + t) * h + g) * D + c16 * 8, t < len_k, v);
-    }
-    // K operands (A of S^T = K . Q^T): token t0 + tt*16 + l16, dims 32*ks + 8*q4.
-    uint4 kr[4][KS];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int t = t0 + tt * 16 + l16;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kr[tt][ks] = load16_if(k + ((k_begin + t) * h + g) * D + 32 * ks + 8 * q4, t < len_k, k);
-    }
-#pragma unroll
-    for (int x = 0; x < VLOADS; ++x) {
-        const int ci = x * 64 + lane;
-        const int tok = ci / CPR, c16 = ci % CPR;
-        *reinterpret_cast<uint4 *>(vlds + tok * VTile<D>::ROWB + c16 * 16) = vr[x];
-    }
-
-    f32x4 s[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s[tt] = mfma16x16x32(as_bf16x8(kr[tt][ks]), qop[ks], s[tt]);
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + tt * 16 + 4 * q4 + i;
-            float x = s[tt][i] * c2;
-            x = (t <= p && t < len_k) ? x : -INFINITY;
-            s[tt][i] = x;
-            mloc = fmaxf(mloc, x);
-        }
-    mloc = max_xor16(mloc);
-    mloc = max_xor32(mloc);
-    const float m_new = fmaxf(acc.m, mloc);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2f(acc.m - m_use);
-    acc.m = m_new;
-    float lsum = 0.0f;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float e = exp2f(s[tt][i] - m_use);
-            s[tt][i] = e;
-            lsum += e;
-        }
-    acc.l = acc.l * alpha + lsum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc.o[dt] *= alpha;
-
-    wave_lds_sync();   // V tile visible to the whole wave
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        // B = P^T: slots 8*q4 + i <- token 32*s2 + 4*q4 + i, slots 8*q4 + 4 + i <- token 32*s2 + 16 + 4*q4 + i.
-        // P is split into a bf16 head and a bf16 tail (p = hi + lo + O(2^-17 p)), so the
-        // probabilities keep float32-like accuracy even when only a few tokens are visible.
-        float pv[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pv[i] = s[2 * s2][i];
-            pv[4 + i] = s[2 * s2 + 1][i];
-        }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hi[i] = split_bf16x2(pv[2 * i], pv[2 * i + 1], &lo[i]);
-        const bf16x8 pop_hi = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
-        const bf16x8 pop_lo = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
-        const int tok_a = 32 * s2 + 4 * q4 + (l16 >> 2);
-        const int tok_b = tok_a + 16;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int col = dt * 16 + 4 * (l16 & 3);
-            const i16x4 va = lds_read_tr16(vlds + tok_a * VTile<D>::ROWB + col * 2);
-            const i16x4 vb = lds_read_tr16(vlds + tok_b * VTile<D>::ROWB + col * 2);
-            const uint2 xa = __builtin_bit_cast(uint2, va), xb = __builtin_bit_cast(uint2, vb);
-            const uint4 au = {xa.x, xa.y, xb.x, xb.y};
-            acc.o[dt] = mfma16x16x32(as_bf16x8(au), pop_hi, acc.o[dt]);
-            acc.o[dt] = mfma16x16x32(as_bf16x8(au), pop_lo, acc.o[dt]);
-        }
-    }
-    wave_lds_sync();   // reads of the V tile done before the next sub-block overwrites it
-}
 
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 (&qop)[D / 32], const uint16_t *q, size_t row, int H, int head0, int G) {
@@ -156,28 +54,157 @@ __device__ __forceinline__ void load_q(bf16x8 (&qop)[D / 32], const uint16_t *q,
     for (int ks = 0; ks < D / 32; ++ks) qop[ks] = as_bf16x8(load16_if(src + 32 * ks, ok, q));
 }
 
-template <int D>
-__device__ __forceinline__ void init_acc(Acc<D> &acc) {
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc.m = -INFINITY;
-    acc.l = 0.0f;
-}
-
 // Sum the 4 per-lane partials of each head.
 __device__ __forceinline__ float head_total(float l) {
     l = sum_xor16(l);
     return sum_xor32(l);
 }
 
+// K and V rows of one sub-block.  Every load instruction reads whole lines
+// (lane i takes the i-th 16-byte chunk of 4 consecutive 256-byte rows), which
+// streams markedly faster than operand-shaped loads; rows are re-laid out
+// through LDS.  t0 is wave-uniform: the base address is scalar and lanes add
+// 32-bit offsets.  Tokens past the sequence end read as zeros.
+template <int D>
+__device__ __forceinline__ void load_kv(uint4 (&kr)[DecodeLds<D>::CH], uint4 (&vr)[DecodeLds<D>::CH],
+                                        const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, size_t k_begin,
+                                        int len_k, int t0, int h, int g) {
+    constexpr int CPR = D / 8;
+    const int lane = lane_id();
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    const size_t base = ((k_begin + t0) * h + g) * D;
+    const bool inside = t0 + kSub <= len_k;
+#pragma unroll
+    for (int x = 0; x < DecodeLds<D>::CH; ++x) {
+        const int ci = x * 64 + lane;
+        const int tok = ci / CPR, c16 = ci % CPR;
+        const uint32_t off = (uint32_t)(tok * h * D + c16 * 8);
+        if (inside) {
+            kr[x] = load16(k + base + off);
+            vr[x] = load16(v + base + off);
+        } else {
+            kr[x] = load16_if(k + base + off, t0 + tok < len_k, k);
+            vr[x] = load16_if(v + base + off, t0 + tok < len_k, v);
+        }
+    }
+}
 
-// ---------------------------------------------------------------- decode
+template <int D>
+__device__ __forceinline__ void store_kv(const uint4 (&kr)[DecodeLds<D>::CH], const uint4 (&vr)[DecodeLds<D>::CH],
+                                         char *klds, char *vlds) {
+    constexpr int CPR = D / 8;
+    const int lane = lane_id();
+#pragma unroll
+    for (int x = 0; x < DecodeLds<D>::CH; ++x) {
+        const int ci = x * 64 + lane;
+        const int tok = ci / CPR, c16 = ci % CPR;
+        *reinterpret_cast<uint4 *>(klds + tok * DecodeLds<D>::KROW + c16 * 16) = kr[x];
+        *reinterpret_cast<uint4 *>(vlds + tok * DecodeLds<D>::VROW + c16 * 16) = vr[x];
+    }
+}
+
+// S^T = K . Q^T for the sub-block in LDS (A = K rows: token tt*16 + l%16,
+// dims 32*ks + 8*(l/16)).
+template <int D>
+__device__ __forceinline__ void qk_sub(f32x4 (&s)[kTT], const char *klds, const bf16x8 (&qop)[D / 32]) {
+    const int lane = lane_id();
+    const int q4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(klds + (tt * 16 + l16) * DecodeLds<D>::KROW +
+                                                               (32 * ks + 8 * q4) * 2);
+            s[tt] = mfma16x16x32(a, qop[ks], s[tt]);
+        }
+    }
+}
+
+// Online-softmax update with the scores of one sub-block starting at token t0
+// (scores become probabilities in place; O is rescaled).
+template <int D>
+__device__ __forceinline__ void softmax_sub(Acc<D> &acc, f32x4 (&s)[kTT], int len_k, int p, int t0, float c2) {
+    const int lane = lane_id();
+    const int q4 = lane >> 4;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + tt * 16 + 4 * q4 + i;
+            float x = s[tt][i] * c2;
+            x = (t <= p && t < len_k) ? x : -INFINITY;
+            s[tt][i] = x;
+            mloc = fmaxf(mloc, x);
+        }
+    mloc = max_xor32(max_xor16(mloc));
+    const float m_new = fmaxf(acc.m, mloc);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = exp2f(acc.m - m_use);
+    acc.m = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e = exp2f(s[tt][i] - m_use);
+            s[tt][i] = e;
+            lsum += e;
+        }
+    acc.l = acc.l * alpha + lsum;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc.o[dt] *= alpha;
+}
+
+// O^T += V^T . P^T over the 32 tokens 32*s2 .. 32*s2+31 of the sub-block, V read
+// from LDS with the transposing read.
+template <int D>
+__device__ __forceinline__ void pv_half(Acc<D> &acc, const f32x4 (&s)[kTT], const char *vlds, int s2) {
+    constexpr int DT = D / 16;
+    using L = DecodeLds<D>;
+    const int lane = lane_id();
+    const int q4 = lane >> 4, l16 = lane & 15;
+    // B = P^T: slots 8*q4 + i <- token 32*s2 + 4*q4 + i, slots 8*q4 + 4 + i <- token 32*s2 + 16 + 4*q4 + i.
+    // P is split into a bf16 head and a bf16 tail (p = hi + lo + O(2^-17 p)), so the
+    // probabilities keep float32-like accuracy even when only a few tokens are visible.
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pv[i] = s[2 * s2][i];
+        pv[4 + i] = s[2 * s2 + 1][i];
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi[i] = split_bf16x2(pv[2 * i], pv[2 * i + 1], &lo[i]);
+    const bf16x8 pop_hi = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
+    const bf16x8 pop_lo = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
+    const int tok_a = 32 * s2 + 4 * q4 + (l16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const int col = dt * 16 + 4 * (l16 & 3);
+        const i16x4 va = lds_read_tr16(vlds + tok_a * L::VROW + col * 2);
+        const i16x4 vb = lds_read_tr16(vlds + (tok_a + 16) * L::VROW + col * 2);
+        const uint2 xa = __builtin_bit_cast(uint2, va), xb = __builtin_bit_cast(uint2, vb);
+        const bf16x8 vop = as_bf16x8(uint4{xa.x, xa.y, xb.x, xb.y});
+        acc.o[dt] = mfma16x16x32(vop, pop_hi, acc.o[dt]);
+        acc.o[dt] = mfma16x16x32(vop, pop_lo, acc.o[dt]);
+    }
+}
+
+// One wave per (split, group, sequence): attend its share of the selected
+// blocks; write the partial output (normalised) and its log2-sum-exp.
+// The current sub-block sits in LDS while the next one's loads are in flight.
 template <int D, int B>
-__global__ __launch_bounds__(64) void attn_decode_split(
+__global__ __launch_bounds__(64, 2) void attn_decode_split(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
     int H, int h, int top_k, int per_split, float c2, float *__restrict__ part_o, float *__restrict__ part_lse) {
-    __shared__ __attribute__((aligned(16))) char vlds[VTile<D>::BYTES];
+    using L = DecodeLds<D>;
+    constexpr int NSUB = B / kSub;
+    __shared__ __attribute__((aligned(16))) char klds[L::KBYTES];
+    __shared__ __attribute__((aligned(16))) char vlds[L::VBYTES];
+    __shared__ int list[kChunk * NSUB];
     const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int nsplit = gridDim.x;
     const int G = H / h;
@@ -185,25 +212,63 @@ __global__ __launch_bounds__(64) void attn_decode_split(
     const size_t k_begin = (size_t)cu_k[s];
     const int len_k = cu_k[s + 1] - cu_k[s];
     const int p = len_k - 1;
+    const int lane = lane_id();
 
     bf16x8 qop[D / 32];
     load_q<D>(qop, q, (size_t)row, H, g * G, G);
     Acc<D> acc;
-    init_acc<D>(acc);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.m = -INFINITY;
+    acc.l = 0.0f;
+
     const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
     const int a0 = split * per_split, a1 = min(top_k, a0 + per_split);
-    for (int a = a0; a < a1; ++a) {
-        const int j = sel[a];
-        if (j < 0 || j > p / B) continue;   // unused slot (or an id outside the causal range)
+    // Sub-block i sits in LDS (K and V) while the next two are in flight in
+    // two register sets (A, B), 32 KB per wave; two waves share a SIMD.
+    uint4 kA[L::CH], vA[L::CH], kB[L::CH], vB[L::CH];
+    f32x4 sc[kTT];
+    for (int c0 = a0; c0 < a1; c0 += kChunk) {
+        // Sub-block starts of this chunk's valid, causal ids (any id order).
+        const int a = c0 + lane;
+        const int j = a < a1 ? sel[a] : -1;
+        int n = 0;
 #pragma unroll
-        for (int sb = 0; sb < B / kSub; ++sb) {
-            const int t0 = j * B + sb * kSub;
-            if (t0 > p) break;
-            attend_sub<D>(acc, qop, k, v, k_begin, len_k, p, t0, h, g, c2, vlds);
+        for (int sb = 0; sb < NSUB; ++sb) {
+            const bool ok = j >= 0 && j <= p / B && j * B + sb * kSub <= p;
+            const unsigned long long bal = __ballot(ok);
+            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+            if (ok) list[n + pos] = j * B + sb * kSub;
+            n += __builtin_popcountll(bal);
+        }
+        wave_lds_sync();
+        if (n == 0) continue;
+        load_kv<D>(kA, vA, k, v, k_begin, len_k, list[0], h, g);
+        if (n > 1) load_kv<D>(kB, vB, k, v, k_begin, len_k, list[1], h, g);
+        store_kv<D>(kA, vA, klds, vlds);
+        if (n > 2) load_kv<D>(kA, vA, k, v, k_begin, len_k, list[2], h, g);
+        for (int i = 0; i < n; i += 2) {
+            // sub-block i in LDS; set B holds i+1, set A holds i+2
+            wave_lds_sync();
+            qk_sub<D>(sc, klds, qop);
+            softmax_sub<D>(acc, sc, len_k, p, list[i], c2);
+            pv_half<D>(acc, sc, vlds, 0);
+            wave_lds_sync();
+            if (i + 1 >= n) break;
+            store_kv<D>(kB, vB, klds, vlds);
+            if (i + 3 < n) load_kv<D>(kB, vB, k, v, k_begin, len_k, list[i + 3], h, g);
+            // sub-block i+1 in LDS; set A holds i+2, set B holds i+3
+            wave_lds_sync();
+            qk_sub<D>(sc, klds, qop);
+            softmax_sub<D>(acc, sc, len_k, p, list[i + 1], c2);
+            pv_half<D>(acc, sc, vlds, 0);
+            wave_lds_sync();
+            if (i + 2 >= n) break;
+            store_kv<D>(kA, vA, klds, vlds);
+            if (i + 4 < n) load_kv<D>(kA, vA, k, v, k_begin, len_k, list[i + 4], h, g);
         }
     }
     const float l = head_total(acc.l);
-    const int lane = lane_id();
     const int hq = lane & 15, q4 = lane >> 4;
     if (hq < G) {
         const size_t slot = (((size_t)s * H + g * G + hq) * nsplit + split);
@@ -217,11 +282,14 @@ __global__ __launch_bounds__(64) void attn_decode_split(
     }
 }
 
-// One wave per (sequence, head): O = sum_s w_s O_s / sum_s w_s, w_s = 2^(lse_s - max).
+// One wave per (sequence, head): O = sum_s w_s O_s / sum_s w_s with
+// w_s = 2^(lse_s - max).  Split weights go through LDS; the d columns are
+// spread over the lanes and every split's row is an independent load.
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_merge(const float *__restrict__ part_o,
                                                         const float *__restrict__ part_lse, int H, int nsplit,
                                                         uint16_t *__restrict__ out, float *__restrict__ lse) {
+    __shared__ float wsh[256];
     const int head = blockIdx.x, s = blockIdx.y;
     const int lane = lane_id();
     const size_t base = ((size_t)s * H + head) * nsplit;
@@ -229,24 +297,44 @@ __global__ __launch_bounds__(64) void attn_decode_merge(const float *__restrict_
     for (int x = lane; x < nsplit; x += 64) m = fmaxf(m, part_lse[base + x]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    float wsum = 0.f;
+    for (int x = lane; x < nsplit; x += 64) {
+        const float ls = part_lse[base + x];
+        const float w = (ls == -INFINITY) ? 0.f : exp2f(ls - m);
+        wsh[x] = w;
+        wsum += w;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
+    wave_lds_sync();
     constexpr int PER = D / 64;
     float o[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
-    float wsum = 0.f;
-    for (int x = 0; x < nsplit; ++x) {
-        const float ls = part_lse[base + x];
-        if (ls == -INFINITY) continue;
-        const float w = exp2f(ls - m);
-        wsum += w;
-        const float *src = part_o + (base + x) * D;
+    const float *src = part_o + base * D + lane * PER;
+    int x = 0;
+    for (; x + 4 <= nsplit; x += 4) {
+        float t[4][PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) o[i] += w * src[lane * PER + i];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) t[u][i] = src[(size_t)(x + u) * D + i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] += wsh[x + u] * t[u][i];
     }
+    for (; x < nsplit; ++x)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += wsh[x] * src[(size_t)x * D + i];
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
     uint16_t *dst = out + ((size_t)s * H + head) * D + lane * PER;
+    if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(o[0] * inv, o[1] * inv);
+    } else {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) dst[i] = (uint16_t)f32_to_bf16_rne(o[i] * inv);
+        for (int i = 0; i < PER; ++i) dst[i] = (uint16_t)(pack_bf16x2(o[i] * inv, 0.f) & 0xffffu);
+    }
     if (lse != nullptr && lane == 0)
         lse[(size_t)s * H + head] = wsum > 0.f ? (m + log2f(wsum)) * 0.69314718055994531f : -INFINITY;
 }
