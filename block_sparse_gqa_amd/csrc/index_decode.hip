@@ -9,7 +9,7 @@
 // touch half lines stream markedly slower on this part.  The block is then
 // re-laid out through a padded per-wave LDS tile into the MFMA operand
 // layout.  The next block of the wave is already in flight in registers while
-// the current one is scored.
+// the current one is scored; blocks are dealt round-robin over the waves.
 //
 // Scores.  Tokens run along the M dimension of v_mfma_f32_16x16x32_bf16 and
 // the h groups along N, so each lane holds 4 tokens of one group per 16-token
@@ -35,7 +35,7 @@ template <int DI, int B>
 __global__ __launch_bounds__(256) void index_decode_blockmax(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int h,
-    float *__restrict__ scores, int e_stride, int blocks_per_wg) {
+    float *__restrict__ scores, int e_stride) {
     using T = IdxTile<DI, B>;
     constexpr int KS = DI / 32;   // 32-dim k-steps
     constexpr int TT = B / 16;    // 16-token tiles per block
@@ -46,11 +46,11 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     const int k_begin = cu_k[s], len_k = cu_k[s + 1] - k_begin;
     const int p = len_k - 1;
     const int E = p / B + 1;
-    const int j_begin = blockIdx.x * blocks_per_wg;
-    if (j_begin >= E) return;
-    const int j_end = min(E, j_begin + blocks_per_wg);
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Blocks are dealt out round-robin over every wave of the sequence, so the
+    // waves in flight at any moment read neighbouring blocks.
+    const int nwaves = gridDim.x * kWaves;
+    const int j_first = blockIdx.x * kWaves + wave;
     const int g = lane & 15, q4 = lane >> 4;
     char *my = tile[wave];
 
@@ -73,11 +73,11 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     };
 
     uint4 cur[T::LOADS], nxt[T::LOADS];
-    int j = j_begin + wave;
-    if (j < j_end) load_block(cur, j);
-    for (; j < j_end; j += kWaves) {
-        const bool more = j + kWaves < j_end;
-        if (more) load_block(nxt, j + kWaves);
+    int j = j_first;
+    if (j < E) load_block(cur, j);
+    for (; j < E; j += nwaves) {
+        const bool more = j + nwaves < E;
+        if (more) load_block(nxt, j + nwaves);
         // registers -> LDS (token-major, padded rows)
 #pragma unroll
         for (int x = 0; x < T::LOADS; ++x) {
@@ -115,14 +115,14 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
 
 template <int DI, int B>
 hipError_t launch(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx, float *scores, hipStream_t st) {
+    // about 2048 workgroups in all, each wave taking every nwaves-th block
     const int e_max = (s.max_k + s.B - 1) / s.B;
-    long total_blocks = (long)e_max * s.num_seqs;
-    int bpw = (int)((total_blocks + 2047) / 2048);
-    bpw = (bpw + 3) / 4 * 4;
-    bpw = bpw < 4 ? 4 : (bpw > 64 ? 64 : bpw);
-    dim3 grid((e_max + bpw - 1) / bpw, s.num_seqs);
+    int per_seq = (2048 + s.num_seqs - 1) / s.num_seqs;
+    const int need = (e_max + kWaves - 1) / kWaves;
+    if (per_seq > need) per_seq = need;
+    dim3 grid(per_seq, s.num_seqs);
     hipLaunchKernelGGL((index_decode_blockmax<DI, B>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q, s.cu_k, s.h,
-                       scores, score_stride(s), bpw);
+                       scores, score_stride(s));
     return hipGetLastError();
 }
 
