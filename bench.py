@@ -68,32 +68,68 @@ def algorithmic(inp, dp, ids):
                 selected_tokens=tok_sel)
 
 
-def cpu_baseline(inputs, sample_rows=192, seed=7):
-    """The oracle (untuned) on a bounded sample of the step, scaled to tokens/s."""
+def cpu_baseline(inputs, budget_s=24.0, seed=7):
+    """The oracle (untuned) on a bounded sample of the step, scaled to tokens/s.
+
+    Workloads share the time budget in order, each taking an even share of what
+    is left.  Decode: whole sequences, in order (at least one).  Prefill: chunks
+    of 256 uniformly drawn rows.  Each part is extrapolated linearly to its full
+    workload.
+    """
     import oracle
     oracle.build(force=False)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
-    parts, secs = [], 0.0
-    for name, inp in inputs.items():
+    parts, secs, spent = [], 0.0, 0.0
+    for n_done, (name, inp) in enumerate(inputs.items()):
+        share = (budget_s - spent) / (len(inputs) - n_done)
         wl = inp.wl
         if wl.is_decode:
-            rows = np.array([0], dtype=np.int64)         # one of the sequences
-            scale = wl.total_q / 1.0
-            desc = f"{name}: 1 of {wl.total_q} sequences"
+            units = [np.array([r], dtype=np.int64) for r in range(wl.total_q)]
+            what = "sequences"
         else:
             rng = np.random.Generator(np.random.PCG64(seed))
-            rows = np.sort(rng.choice(wl.total_q, size=min(sample_rows, wl.total_q), replace=False))
-            scale = wl.total_q / len(rows)
-            desc = f"{name}: {len(rows)} uniformly drawn rows of {wl.total_q}"
-        t0 = time.perf_counter()
-        ids, _, _ = oracle.index_topk(inp, rows, threads=threads)
-        oracle.sparse_attention(inp, ids, rows, threads=threads)
-        dt = time.perf_counter() - t0
-        secs += dt * scale
-        parts.append(f"{desc} ({dt:.1f} s)")
+            perm = rng.permutation(wl.total_q).astype(np.int64)
+            units = [np.sort(perm[i:i + 256]) for i in range(0, wl.total_q, 256)]
+            what = "uniformly drawn rows"
+        done, dt = 0, 0.0
+        for rows in units:
+            t0 = time.perf_counter()
+            ids, _, _ = oracle.index_topk(inp, rows, threads=threads)
+            oracle.sparse_attention(inp, ids, rows, threads=threads)
+            dt += time.perf_counter() - t0
+            done += len(rows)
+            if dt >= share:
+                break
+        spent += dt
+        secs += dt * wl.total_q / done
+        parts.append(f"{name}: {done} of {wl.total_q} {what} in {dt:.1f} s")
     tokens = sum(inp.wl.total_q for inp in inputs.values())
     return {"value": tokens / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(parts) + "; extrapolated linearly to the full step"}
+            "sample": "; ".join(parts) + "; each part extrapolated linearly to its full workload"}
+
+
+def measured_traffic(kernel_file, symbol, launches_per_call):
+    """HBM bytes per call of the dominant kernel from the committed PMC summary.
+
+    The summary records FETCH_SIZE / WRITE_SIZE per dispatch, the scale factors
+    a plain copy of known size gives for the same counters, and the SHA-256 of
+    the kernel source the counters were taken on.  If that source has changed
+    since, the counters no longer describe the kernel and None is returned.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    src = os.path.join(ROOT, "block_sparse_gqa_amd", "csrc", kernel_file)
+    try:
+        with open(path) as f:
+            table = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    for e in table.get("kernels", []):
+        if e.get("symbol") == symbol and e.get("source_sha256") == digest:
+            return e["bytes_per_dispatch"] * launches_per_call
+    return None
 
 
 def main():
@@ -184,8 +220,8 @@ def main():
             r.update({"bound": "hbm", "algorithmic_GB": (alg["index_bytes"] + alg["attn_bytes"]) / 1e9,
                       "GB_per_s": tot, "frac_hbm_peak": tot / HBM_PEAK_GBS,
                       "index_topk_GB_per_s": gbs_i, "sparse_attn_GB_per_s": gbs_a})
-            kernels.append(("msa_index_topk[%s]" % name, t_idx, "hbm", alg["index_bytes"]))
-            kernels.append(("msa_sparse_attn_decode[%s]" % name, t_att, "hbm", alg["attn_bytes"]))
+            kernels.append(("msa_index_topk[%s]" % name, t_idx, "hbm", alg["index_bytes"], None))
+            kernels.append(("msa_sparse_attn_decode[%s]" % name, t_att, "hbm", alg["attn_bytes"], None))
         else:
             tf_i = alg["index_flops"] / (t_idx * 1e-3) / 1e12
             tf_a = alg["attn_flops"] / (t_att * 1e-3) / 1e12
@@ -193,17 +229,20 @@ def main():
             r.update({"bound": "mfma", "algorithmic_TFLOP": (alg["index_flops"] + alg["attn_flops"]) / 1e12,
                       "TFLOP_per_s": tot, "frac_mfma_peak": tot / MFMA_BF16_PEAK_TFLOPS,
                       "index_topk_TFLOP_per_s": tf_i, "sparse_attn_TFLOP_per_s": tf_a})
-            kernels.append(("msa_index_topk[%s]" % name, t_idx, "mfma", alg["index_flops"]))
-            kernels.append(("msa_sparse_attn_prefill[%s]" % name, t_att, "mfma", alg["attn_flops"]))
+            kernels.append(("msa_index_topk[%s]" % name, t_idx, "mfma", alg["index_flops"], None))
+            # one launch of attn_prefill_tile per call
+            kernels.append(("msa_sparse_attn_prefill[%s]" % name, t_att, "mfma", alg["attn_flops"],
+                            ("attn_prefill.hip", "attn_prefill_tile", 1)))
         results[name] = r
 
-    kname, kms, kbound, kwork = max(kernels, key=lambda x: x[1])
+    kname, kms, kbound, kwork, ksrc = max(kernels, key=lambda x: x[1])
     if kbound == "hbm":
         achieved, peak, unit = kwork / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         achieved, peak, unit = kwork / (kms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     roofline = {"bound": kbound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": None, "avg_launch_ms": kms}
+                "frac": achieved / peak, "traffic": measured_traffic(*ksrc) if ksrc else None,
+                "traffic_unit": "bytes per launch", "avg_launch_ms": kms}
 
     cpu = None
     if not args.no_cpu_baseline:
