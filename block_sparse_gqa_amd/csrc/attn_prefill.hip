@@ -11,14 +11,16 @@
 // 64-token K and V sub-blocks.
 //
 // Staging.  A 4-stage LDS ring is filled with direct global->LDS loads
-// (global_load_lds_dwordx4: lane i of a load writes base + 16*i), so three
+// (global_load_lds_dwordx4: lane i of a load writes base + 16*i), so several
 // sub-blocks are in flight per workgroup without holding staging registers.
 // Row strides are padded (K: 2d+16 bytes, V: 2d+64 bytes) so that the K
 // operand reads and the transposing V reads are bank-conflict free; pad
 // slots are filled by the same loads and never read.  Ring reads are issued
 // in inline asm (each block waits for its own results) so the compiler does
-// not serialise them behind the in-flight ring loads; completion of a stage
-// is tracked with explicit vmcnt waits plus a barrier.
+// not serialise them behind the in-flight ring loads.  Stages are handed
+// between waves with LDS flags and counters instead of workgroup barriers
+// (the protocol is described at the loop), so the waves sharing a SIMD drift
+// apart and overlap one another's MFMA and VALU work.
 //
 // Rows.  A row is one (query, head) pair.  Each of the NW waves owns RT fixed row tiles
 // of 16 rows (16/G queries x G heads) whose O accumulators, running max and
@@ -44,6 +46,8 @@ typedef __attribute__((address_space(1))) void gbl_void;
 
 constexpr int kWin = 256;    // key blocks per union window (one per thread)
 constexpr int kStages = 4;   // ring depth (sub-blocks)
+// Fourth word of a raw buffer resource (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int D>
 struct Ring {
@@ -56,20 +60,6 @@ struct Ring {
     static constexpr int KBYTES = 64 * KROW;
     static constexpr int VBYTES = 64 * VROW;
     static constexpr int STAGE = KBYTES + VBYTES;
-    // loads issued per sub-block by wave w of NW (instructions i = w, w+NW, ...)
-    template <int NW>
-    static constexpr int per_wave(int w) { return (KINSTR - w + NW - 1) / NW + (VINSTR - w + NW - 1) / NW; }
-    // waves fall into at most three classes of equal per-wave counts
-    template <int NW>
-    static constexpr int wave_class(int w) {
-        return per_wave<NW>(w) == per_wave<NW>(0) ? 0 : (per_wave<NW>(w) == per_wave<NW>(NW - 1) ? 2 : 1);
-    }
-    template <int NW>
-    static constexpr int class_rep(int c) {
-        for (int w = 0; w < NW; ++w)
-            if (wave_class<NW>(w) == c) return w;
-        return NW - 1;
-    }
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
@@ -84,46 +74,81 @@ __device__ __forceinline__ void wait_vm() {
 // output register must never alias the address input that later reads in the
 // same block still use.
 
-// Four 16-byte K operand reads (k-steps 0..3, 64 bytes apart), one wait.
-__device__ __forceinline__ void lds_k4(uint4 &a0, uint4 &a1, uint4 &a2, uint4 &a3, uint32_t addr) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:64\n\t"
-        "ds_read_b128 %2, %4 offset:128\n\t"
-        "ds_read_b128 %3, %4 offset:192\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-        : "v"(addr)
-        : "memory");
-}
-__device__ __forceinline__ void lds_k2(uint4 &a0, uint4 &a1, uint32_t addr) {
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %2 offset:64\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a0), "=&v"(a1)
-        : "v"(addr)
-        : "memory");
+// K operands of two 16-token tiles (rows tok and tok + 16, all k-steps of
+// 32 dims, 64 bytes apart), one wait.  ROW16 = 16 rows in bytes.
+template <int KS, int ROW16>
+__device__ __forceinline__ void lds_k_pair(uint4 (&a)[2 * KS], uint32_t addr) {
+    if constexpr (KS == 4) {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:64\n\t"
+            "ds_read_b128 %2, %8 offset:128\n\t"
+            "ds_read_b128 %3, %8 offset:192\n\t"
+            "ds_read_b128 %4, %8 offset:%9\n\t"
+            "ds_read_b128 %5, %8 offset:%9+64\n\t"
+            "ds_read_b128 %6, %8 offset:%9+128\n\t"
+            "ds_read_b128 %7, %8 offset:%9+192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+            : "v"(addr), "i"(ROW16)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %4 offset:64\n\t"
+            "ds_read_b128 %2, %4 offset:%5\n\t"
+            "ds_read_b128 %3, %4 offset:%5+64\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+            : "v"(addr), "i"(ROW16)
+            : "memory");
+    }
 }
 
-// Transposing V reads for 4 consecutive 16-column d-tiles: for each, rows
-// tok and tok + 16 (offset ROW16 bytes), columns 32 bytes apart.
-template <int OFF, int ROW16>
-__device__ __forceinline__ void lds_v4(i16x4 (&va)[4], i16x4 (&vb)[4], uint32_t addr) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(va[0]), "=&v"(vb[0]), "=&v"(va[1]), "=&v"(vb[1]), "=&v"(va[2]), "=&v"(vb[2]), "=&v"(va[3]), "=&v"(vb[3])
-        : "v"(addr), "i"(OFF), "i"(OFF + ROW16), "i"(OFF + 32), "i"(OFF + 32 + ROW16), "i"(OFF + 64),
-          "i"(OFF + 64 + ROW16), "i"(OFF + 96), "i"(OFF + 96 + ROW16)
-        : "memory");
+// Transposing V reads of one 32-token half for every 16-column d-tile: rows
+// tok and tok + 16 (ROW16 bytes apart), d-tiles 32 bytes apart, one wait.
+template <int DT, int ROW16>
+__device__ __forceinline__ void lds_v_half(i16x4 (&va)[DT], i16x4 (&vb)[DT], uint32_t addr) {
+    if constexpr (DT == 8) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16\n\t"
+            "ds_read_b64_tr_b16 %1, %16 offset:%17\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:32\n\t"
+            "ds_read_b64_tr_b16 %3, %16 offset:%17+32\n\t"
+            "ds_read_b64_tr_b16 %4, %16 offset:64\n\t"
+            "ds_read_b64_tr_b16 %5, %16 offset:%17+64\n\t"
+            "ds_read_b64_tr_b16 %6, %16 offset:96\n\t"
+            "ds_read_b64_tr_b16 %7, %16 offset:%17+96\n\t"
+            "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+            "ds_read_b64_tr_b16 %9, %16 offset:%17+128\n\t"
+            "ds_read_b64_tr_b16 %10, %16 offset:160\n\t"
+            "ds_read_b64_tr_b16 %11, %16 offset:%17+160\n\t"
+            "ds_read_b64_tr_b16 %12, %16 offset:192\n\t"
+            "ds_read_b64_tr_b16 %13, %16 offset:%17+192\n\t"
+            "ds_read_b64_tr_b16 %14, %16 offset:224\n\t"
+            "ds_read_b64_tr_b16 %15, %16 offset:%17+224\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(va[0]), "=&v"(vb[0]), "=&v"(va[1]), "=&v"(vb[1]), "=&v"(va[2]), "=&v"(vb[2]), "=&v"(va[3]),
+              "=&v"(vb[3]), "=&v"(va[4]), "=&v"(vb[4]), "=&v"(va[5]), "=&v"(vb[5]), "=&v"(va[6]), "=&v"(vb[6]),
+              "=&v"(va[7]), "=&v"(vb[7])
+            : "v"(addr), "i"(ROW16)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %8 offset:%9\n\t"
+            "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
+            "ds_read_b64_tr_b16 %3, %8 offset:%9+32\n\t"
+            "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+            "ds_read_b64_tr_b16 %5, %8 offset:%9+64\n\t"
+            "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
+            "ds_read_b64_tr_b16 %7, %8 offset:%9+96\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(va[0]), "=&v"(vb[0]), "=&v"(va[1]), "=&v"(vb[1]), "=&v"(va[2]), "=&v"(vb[2]), "=&v"(va[3]),
+              "=&v"(vb[3])
+            : "v"(addr), "i"(ROW16)
+            : "memory");
+    }
 }
 
 __device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
@@ -137,12 +162,25 @@ __device__ __forceinline__ unsigned long long lds_u64(uint32_t addr) {
     return v;
 }
 
+__device__ __forceinline__ void lds_store_u32(uint32_t addr, int v) {
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
+}
+// One wave-level increment of the counter at addr; returns its prior value
+// (the same in every lane).
+__device__ __forceinline__ int lds_add_rtn_u32(uint32_t addr) {
+    int prior = 0;
+    if ((threadIdx.x & 63) == 0) {
+        asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=&v"(prior) : "v"(addr), "v"(1) : "memory");
+    }
+    return __builtin_amdgcn_readfirstlane(prior);
+}
+
 __device__ __forceinline__ uint4 pack_tr(i16x4 a, i16x4 b) {
     const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
     return uint4{x.x, x.y, y.x, y.y};
 }
 
-template <int D, int RT, int NW>
+template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
@@ -152,15 +190,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
     constexpr int CPR = D / 8;   // data slots per row
+    constexpr float kLazy = 8.0f;   // log2 headroom before the reference max moves
     __shared__ __attribute__((aligned(16))) char ring[kStages * R::STAGE];
     __shared__ unsigned long long masks[kWin];
     __shared__ unsigned long long list_m[kWin];
     __shared__ int list_u[kWin];
+    __shared__ int list_n[kWin];
     __shared__ int wave_cnt[4];
+    __shared__ int ready[kStages];
+    __shared__ int done[kStages];
 
     const int G = H / h;
-    const int Qt = 16 / G;                    // queries per row tile
-    const int Tq = NW * RT * Qt;              // queries per workgroup (<= 64)
+    const int Qt = 16 / G;                    // queries per row tile (one tile per wave)
+    const int Tq = NW * Qt;                   // queries per workgroup (<= 64)
     const int bid = blockIdx.x;
     const int g = bid % h;
     const int rest = bid / h;
@@ -180,120 +222,180 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, q4 = lane >> 4;
 
-    // This lane's row in each of the wave's row tiles.
-    bf16x8 qop[RT][KS];
-    int prow[RT], qbit[RT];
-    f32x4 o[RT][DT];
-    float m[RT], l[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int qi = l16 / G, head = l16 % G;
-        const int qidx = (wave * RT + rt) * Qt + qi;
-        const bool ok = (l16 < Qt * G) && (qidx < tq_valid);
-        prow[rt] = ok ? shift + r0 + qidx : -1;
-        qbit[rt] = qidx;
+    // This lane's row (query qi of the wave's tile, head `head` of the group).
+    const int qi = l16 / G, head = l16 % G;
+    const int qidx = wave * Qt + qi;
+    const bool row_ok = (l16 < Qt * G) && (qidx < tq_valid);
+    const int prow = row_ok ? shift + r0 + qidx : -1;
+    const int p_first = shift + r0 + wave * Qt;   // smallest position of the wave's queries
+    const int p_wave_last = shift + r0 + min(wave * Qt + Qt, tq_valid) - 1;
+    bf16x8 qop[KS];
+    {
         const uint16_t *src = q + ((size_t)(q_begin + r0 + qidx) * H + g * G + head) * D + 8 * q4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = as_bf16x8(load16_if(src + 32 * ks, ok, q));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m[rt] = -INFINITY;
-        l[rt] = 0.0f;
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(load16_if(src + 32 * ks, row_ok, q));
     }
-    const unsigned long long tile_bits = (1ull << Qt) - 1ull;
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY;   // reference max (log2 units) the exponentials are taken against
+    float l = 0.0f;
+    const unsigned long long tile_bits = ((1ull << Qt) - 1ull) << (wave * Qt);
 
     const uint32_t ring0 = lds_addr(ring);
-    const uint32_t list_u0 = lds_addr(list_u), list_m0 = lds_addr(list_m);
+    const uint32_t list_u0 = lds_addr(list_u), list_m0 = lds_addr(list_m), list_n0 = lds_addr(list_n);
+    const uint32_t ready0 = lds_addr(ready), done0 = lds_addr(done);
     // Per-lane read offsets inside a stage.
     const uint32_t k_rd = (uint32_t)(l16 * R::KROW + q4 * 16);
     const uint32_t v_rd = (uint32_t)(R::KBYTES + (4 * q4 + (l16 >> 2)) * R::VROW + 8 * (l16 & 3));
 
-    // Direct global->LDS loads of one 64-token sub-block into a ring stage.
-    // Each lane's element offset inside a sub-block is fixed per load slot and
-    // computed once.  Pad slots read chunk 0 of their own row; for a sub-block
-    // that runs past the sequence end, rows are clamped to the last valid
-    // token (finite data, masked later), so no lane leaves the sequence.
-    constexpr int KI = (R::KINSTR + NW - 1) / NW, VI = (R::VINSTR + NW - 1) / NW;
-    uint32_t koff[KI], voff[VI];
-#pragma unroll
-    for (int ii = 0; ii < KI; ++ii) {
-        const int slot = (ii * NW + wave) * 64 + lane;
-        const int row = slot / R::KSLOT_ROW, c16 = slot % R::KSLOT_ROW;
-        koff[ii] = (uint32_t)(row * h * D + (c16 < CPR ? c16 : 0) * 8);
-    }
-#pragma unroll
-    for (int ii = 0; ii < VI; ++ii) {
-        const int slot = (ii * NW + wave) * 64 + lane;
-        const int row = slot / R::VSLOT_ROW, c16 = slot % R::VSLOT_ROW;
-        voff[ii] = (uint32_t)(row * h * D + (c16 < CPR ? c16 : 0) * 8);
-    }
-    auto issue = [&](int t0, int stage) {
+    // Direct loads of one 64-token sub-block into a ring stage, all issued by
+    // one wave: lane i of load instruction n fills 16-byte slot 64n + i of the
+    // stage's K (then V) rows.  The loads go through a buffer resource that
+    // ends at the sequence's last token, so rows past it read as zeros (they
+    // are masked later) and pad slots, given an out-of-range offset, move no
+    // data at all.
+    auto issue_all = [&](int t0_in, int stage_in) {
+        const int t0 = __builtin_amdgcn_readfirstlane(t0_in);
+        const int stage = __builtin_amdgcn_readfirstlane(stage_in);
+        const int hd2 = h * D * 2;
+        const size_t row0 = ((k_begin + t0) * h + g) * D;
+        const int nrec = (len_k - 1 - t0) * hd2 + 2 * D;   // through the last token's row of group g
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void *)(k + row0), 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void *)(v + row0), 0, nrec, kRsrcWord3);
         char *base = ring + stage * R::STAGE;
-        const bool inside = t0 + 63 < len_k;
-        const size_t tok0 = (k_begin + t0) * h + g;
-        const uint16_t *kb = k + tok0 * D, *vb = v + tok0 * D;
+        // recomputed per call (kept out of registers across the loop)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        {
+            int row = ln / R::KSLOT_ROW, c16 = ln % R::KSLOT_ROW;
 #pragma unroll
-        for (int ii = 0; ii < KI; ++ii) {
-            const int i = ii * NW + wave;
-            if (i < R::KINSTR) {
-                const uint16_t *src = kb + koff[ii];
-                if (!inside) {
-                    const int slot = i * 64 + lane;
-                    const int row = slot / R::KSLOT_ROW, c16 = slot % R::KSLOT_ROW;
-                    const int t = min(t0 + row, len_k - 1);
-                    src = k + ((k_begin + t) * h + g) * D + (c16 < CPR ? c16 : 0) * 8;
+            for (int i = 0; i < R::KINSTR; ++i) {
+                const int off = c16 < CPR ? row * hd2 + c16 * 16 : 0x7fffffff;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(base + i * 1024), 16, off, 0, 0, 0);
+                row += 64 / R::KSLOT_ROW;
+                c16 += 64 % R::KSLOT_ROW;
+                if (c16 >= R::KSLOT_ROW) {
+                    c16 -= R::KSLOT_ROW;
+                    ++row;
                 }
-                __builtin_amdgcn_global_load_lds((const gbl_void *)src, (lds_void *)(base + i * 1024), 16, 0, 0);
             }
         }
+        {
+            int row = ln / R::VSLOT_ROW, c16 = ln % R::VSLOT_ROW;
 #pragma unroll
-        for (int ii = 0; ii < VI; ++ii) {
-            const int i = ii * NW + wave;
-            if (i < R::VINSTR) {
-                const uint16_t *src = vb + voff[ii];
-                if (!inside) {
-                    const int slot = i * 64 + lane;
-                    const int row = slot / R::VSLOT_ROW, c16 = slot % R::VSLOT_ROW;
-                    const int t = min(t0 + row, len_k - 1);
-                    src = v + ((k_begin + t) * h + g) * D + (c16 < CPR ? c16 : 0) * 8;
+            for (int i = 0; i < R::VINSTR; ++i) {
+                const int off = c16 < CPR ? row * hd2 + c16 * 16 : 0x7fffffff;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(base + R::KBYTES + i * 1024), 16, off, 0, 0, 0);
+                row += 64 / R::VSLOT_ROW;
+                c16 += 64 % R::VSLOT_ROW;
+                if (c16 >= R::VSLOT_ROW) {
+                    c16 -= R::VSLOT_ROW;
+                    ++row;
                 }
-                __builtin_amdgcn_global_load_lds((const gbl_void *)src, (lds_void *)(base + R::KBYTES + i * 1024), 16,
-                                                 0, 0);
             }
         }
     };
-    // Wait until only the `ahead` sub-blocks issued after this one are still in
-    // flight (per-wave load counts differ: waves issue loads i = w, w+NW, ...).
-    auto wait_stage = [&](int ahead) {
-        const int a = ahead >= 2 ? 2 : ahead;
-        switch (R::template wave_class<NW>(wave) * 3 + a) {
-            case 0: wait_vm<0>(); break;
-            case 1: wait_vm<R::template per_wave<NW>(0)>(); break;
-            case 2: wait_vm<2 * R::template per_wave<NW>(0)>(); break;
-            case 3: wait_vm<0>(); break;
-            case 4: wait_vm<R::template per_wave<NW>(R::template class_rep<NW>(1))>(); break;
-            case 5: wait_vm<2 * R::template per_wave<NW>(R::template class_rep<NW>(1))>(); break;
-            case 6: wait_vm<0>(); break;
-            case 7: wait_vm<R::template per_wave<NW>(R::template class_rep<NW>(2))>(); break;
-            default: wait_vm<2 * R::template per_wave<NW>(R::template class_rep<NW>(2))>(); break;
+
+    // One item for this wave's row tile: the sub-block at t0 staged at sbase;
+    // mk = which queries of the workgroup tile selected its block.
+    auto attend = [&](uint32_t sbase, int t0, unsigned long long mk) {
+        // S^T = K . Q^T for the four 16-token tiles of the sub-block
+        f32x4 sacc[4];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            uint4 a[2 * KS];
+            lds_k_pair<KS, 16 * R::KROW>(a, sbase + k_rd + tp * 32 * R::KROW);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                sacc[2 * tp + u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    sacc[2 * tp + u] = mfma16x16x32(as_bf16x8(a[u * KS + ks]), qop[ks], sacc[2 * tp + u]);
+            }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
+        // Online softmax in log2 units.  A row whose query did not select the
+        // block gets bias +inf (all its weights 0); future tokens are masked
+        // only on diagonal sub-blocks.
+        const bool selected = prow >= 0 && ((mk >> qidx) & 1ull);
+        if (t0 + 63 > p_first) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + tt * 16 + 4 * q4 + i > prow) sacc[tt][i] = -INFINITY;
+        }
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sacc[tt][i]);
+        mloc = max_xor32(max_xor16(mloc)) * c2;
+        // The reference max moves only when the block max exceeds it by more
+        // than kLazy, so weights stay <= 2^kLazy and O is rarely rescaled.
+        const bool move = selected && mloc > m_ref + kLazy;
+        if (__ballot(move) != 0ull) {
+            const float alpha = move ? exp2f(m_ref - mloc) : 1.0f;   // 0 on a row's first block
+            m_ref = move ? mloc : m_ref;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        }
+        const float bias = (selected && m_ref > -INFINITY) ? m_ref : INFINITY;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = exp2f(fmaf(sacc[tt][i], c2, -bias));
+                sacc[tt][i] = e;
+                lsum += e;
+            }
+        l += lsum;
+        // O^T += V^T . P^T, P split into a bf16 head and tail
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            // slots 8*q4 + i <- tile 2*s2 value i, slots 8*q4 + 4 + i <- tile 2*s2+1 value i
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                hi[i] = split_bf16x2(sacc[2 * s2][2 * i], sacc[2 * s2][2 * i + 1], &lo[i]);
+                hi[2 + i] = split_bf16x2(sacc[2 * s2 + 1][2 * i], sacc[2 * s2 + 1][2 * i + 1], &lo[2 + i]);
+            }
+            const bf16x8 p_hi = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8 p_lo = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+            for (int dq = 0; dq < DT / 4; ++dq) {
+                i16x4 va[4], vb[4];
+                lds_v_half<4, 16 * R::VROW>(va, vb, sbase + v_rd + s2 * 32 * R::VROW + dq * 128);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const bf16x8 vop = as_bf16x8(pack_tr(va[x], vb[x]));
+                    o[4 * dq + x] = mfma16x16x32(vop, p_hi, o[4 * dq + x]);
+                    o[4 * dq + x] = mfma16x16x32(vop, p_lo, o[4 * dq + x]);
+                }
+            }
+        }
     };
 
     for (int w0 = 0; w0 < e_tile; w0 += kWin) {
         if (tid < kWin) masks[tid] = 0ull;
+        if (tid < kStages) {
+            ready[tid] = 0;
+            done[tid] = 0;
+        }
         __syncthreads();
         // Which queries of the tile selected which block of this window.
         const int32_t *tile_ids = ids + ((size_t)(q_begin + r0) * h + g) * top_k;
         for (int e = tid; e < tq_valid * top_k; e += 64 * NW) {
-            const int qi = e / top_k, a = e % top_k;
-            const int j = tile_ids[(size_t)qi * h * top_k + a];
-            const int pq = shift + r0 + qi;
-            if (j >= w0 && j < w0 + kWin && j >= 0 && j <= pq / B) atomicOr(&masks[j - w0], 1ull << qi);
+            const int eq = e / top_k, a = e % top_k;
+            const int j = tile_ids[(size_t)eq * h * top_k + a];
+            const int pq = shift + r0 + eq;
+            if (j >= w0 && j < w0 + kWin && j >= 0 && j <= pq / B) atomicOr(&masks[j - w0], 1ull << eq);
         }
         __syncthreads();
-        // Compact the blocks somebody selected, ascending.
+        // Compact the blocks somebody selected, ascending, with the number of
+        // waves whose row tile holds a selecting query.
         const unsigned long long mv = tid < kWin ? masks[tid] : 0ull;
         const unsigned long long bal = __ballot(mv != 0ull);
         const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
@@ -306,160 +408,112 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
             count += wave_cnt[w];
         }
         if (mv != 0ull) {
+            int nact = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) nact += ((mv >> (w * Qt)) & ((1ull << Qt) - 1ull)) != 0ull;
             list_u[base + before] = w0 + tid;
             list_m[base + before] = mv;
+            list_n[base + before] = nact;
         }
         __syncthreads();
 
-        const int nitems = count * nsub;
+        // Items are the 64-token sub-blocks of the listed blocks; a trailing
+        // sub-block that starts after the tile's last query is dropped.
+        int nitems = count * nsub;
+        if (nsub > 1 && count > 0 && (int)lds_u32(list_u0 + 4 * (count - 1)) * B + 64 > p_last) --nitems;
         auto t0_of = [&](int it) {
             return (int)lds_u32(list_u0 + 4 * (it / nsub)) * B + (it % nsub) * 64;
         };
-#pragma unroll
-        for (int x = 0; x < kStages - 1; ++x)
-            if (x < nitems) issue(t0_of(x), x);
-
-        for (int it = 0; it < nitems; ++it) {
-            const int stage = it % kStages;
-            wait_stage(min(kStages - 2, nitems - 1 - it));
-            const int t0 = t0_of(it);
-            const unsigned long long mk = lds_u64(list_m0 + 8 * (it / nsub));
-            const unsigned long long wbits = mk >> (wave * RT * Qt);
-            bool act[RT];
-            bool any = false;
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                act[rt] = ((wbits >> (rt * Qt)) & tile_bits) != 0ull;
-                any |= act[rt];
-            }
-            const uint32_t sbase = ring0 + stage * R::STAGE;
-            if (t0 <= p_last && any) {
-                f32x4 sacc[RT][4];
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    uint4 a[KS];
-                    if constexpr (KS == 4) lds_k4(a[0], a[1], a[2], a[3], sbase + k_rd + tt * 16 * R::KROW);
-                    else lds_k2(a[0], a[1], sbase + k_rd + tt * 16 * R::KROW);
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        if (!act[rt]) continue;
-                        sacc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks)
-                            sacc[rt][tt] = mfma16x16x32(as_bf16x8(a[ks]), qop[rt][ks], sacc[rt][tt]);
-                    }
-                }
-                // online softmax per row (log2 domain)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    if (!act[rt]) continue;
-                    const bool selected = prow[rt] >= 0 && ((mk >> qbit[rt]) & 1ull);
-                    float mloc = -INFINITY;
-#pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int t = t0 + tt * 16 + 4 * q4 + i;
-                            const float x = (selected && t <= prow[rt]) ? sacc[rt][tt][i] * c2 : -INFINITY;
-                            sacc[rt][tt][i] = x;
-                            mloc = fmaxf(mloc, x);
-                        }
-                    mloc = max_xor32(max_xor16(mloc));
-                    const float m_new = fmaxf(m[rt], mloc);
-                    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-                    const float alpha = exp2f(m[rt] - m_use);
-                    m[rt] = m_new;
-                    float lsum = 0.0f;
-#pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float e = exp2f(sacc[rt][tt][i] - m_use);
-                            sacc[rt][tt][i] = e;
-                            lsum += e;
-                        }
-                    l[rt] = l[rt] * alpha + lsum;
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
-                }
-                // O^T += V^T . P^T, P split into bf16 head + tail
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    bf16x8 p_hi[RT], p_lo[RT];
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        if (!act[rt]) continue;
-                        // slots 8*q4 + i <- tile 2*s2 value i, slots 8*q4 + 4 + i <- tile 2*s2+1 value i
-                        float pv[8];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pv[i] = sacc[rt][2 * s2][i];
-                            pv[4 + i] = sacc[rt][2 * s2 + 1][i];
-                        }
-                        uint32_t hi[4], lo[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) hi[i] = split_bf16x2(pv[2 * i], pv[2 * i + 1], &lo[i]);
-                        p_hi[rt] = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
-                        p_lo[rt] = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
-                    }
-#pragma unroll
-                    for (int dq = 0; dq < DT / 4; ++dq) {
-                        i16x4 va[4], vb[4];
-                        const uint32_t addr = sbase + v_rd + s2 * 32 * R::VROW;
-                        if (dq == 0) lds_v4<0, 16 * R::VROW>(va, vb, addr);
-                        else lds_v4<128, 16 * R::VROW>(va, vb, addr);
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            const int dt = dq * 4 + x;
-                            const bf16x8 vop = as_bf16x8(pack_tr(va[x], vb[x]));
-#pragma unroll
-                            for (int rt = 0; rt < RT; ++rt) {
-                                if (!act[rt]) continue;
-                                o[rt][dt] = mfma16x16x32(vop, p_hi[rt], o[rt][dt]);
-                                o[rt][dt] = mfma16x16x32(vop, p_lo[rt], o[rt][dt]);
-                            }
-                        }
-                    }
-                }
-            }
-            // refill the stage read in the previous iteration (every wave is past it)
-            if (it + kStages - 1 < nitems) issue(t0_of(it + kStages - 1), (it + kStages - 1) % kStages);
+        // Ring protocol.  ready[s] holds the stamp (item + 1) of the sub-block
+        // stage s holds once its loads have landed.  Only the waves whose row
+        // tile is active read an item; done[s] counts them, and the last one
+        // (the count reaching the item's active-wave count) clears the counter
+        // and refills the stage with the item kStages ahead.  Its loads are
+        // published after its next item, or before it would block, so no wave
+        // ever waits while holding an unpublished stage.  Waves skip items
+        // they have no work in and run ahead until the ring holds them back.
+        if (wave < kStages && wave < nitems) {
+            issue_all(t0_of(wave), wave);
+            wait_vm<0>();
+            lds_store_u32(ready0 + 4 * wave, wave + 1);
         }
+        int pend_stage = -1, pend_stamp = 0;
+        auto publish = [&]() {
+            if (pend_stage >= 0) {
+                wait_vm<0>();
+                lds_store_u32(ready0 + 4 * pend_stage, pend_stamp);
+                pend_stage = -1;
+            }
+        };
+
+        for (int e0 = 0; e0 < count; e0 += 64) {
+            const unsigned long long m_e = (e0 + lane < count) ? lds_u64(list_m0 + 8 * (e0 + lane)) : 0ull;
+            unsigned long long act = __ballot((m_e & tile_bits) != 0ull);
+            while (act != 0ull) {
+                const int ei = e0 + __builtin_ctzll(act);
+                act &= act - 1ull;
+                const unsigned long long mk = lds_u64(list_m0 + 8 * ei);
+                const int nact = __builtin_amdgcn_readfirstlane((int)lds_u32(list_n0 + 4 * ei));
+                const int blk = __builtin_amdgcn_readfirstlane((int)lds_u32(list_u0 + 4 * ei));
+                for (int sub = 0; sub < nsub; ++sub) {
+                    const int it = ei * nsub + sub;
+                    if (it >= nitems) break;
+                    const int stage = it % kStages;
+                    const int t0 = blk * B + sub * 64;
+                    if (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) != it + 1) {
+                        publish();
+                        while (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) != it + 1)
+                            __builtin_amdgcn_s_sleep(1);
+                    }
+                    const uint32_t sbase = ring0 + stage * R::STAGE;
+                    if (t0 <= p_wave_last) {
+                        attend(sbase, t0, mk);
+                    }
+                    publish();
+                    const int prior = lds_add_rtn_u32(done0 + 4 * stage);
+                    if (prior == nact - 1) {
+                        lds_store_u32(done0 + 4 * stage, 0);
+                        if (it + kStages < nitems) {
+                            issue_all(t0_of(it + kStages), stage);
+                            pend_stage = stage;
+                            pend_stamp = it + kStages + 1;
+                        }
+                    }
+                }
+            }
+        }
+        publish();
         wait_vm<0>();
         __syncthreads();
     }
 
     // Epilogue: normalise and write this wave's rows.
+    const float lt = sum_xor32(sum_xor16(l));
+    if (prow < 0) return;
+    const int row = q_begin + r0 + qidx;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.0f;
+    uint16_t *dst = out + ((size_t)row * H + g * G + head) * D + 4 * q4;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const float lt = sum_xor32(sum_xor16(l[rt]));
-        if (prow[rt] < 0) continue;
-        const int qi = l16 / G, head = l16 % G;
-        const int row = q_begin + r0 + (wave * RT + rt) * Qt + qi;
-        const float inv = lt > 0.f ? 1.0f / lt : 0.0f;
-        uint16_t *dst = out + ((size_t)row * H + g * G + head) * D + 4 * q4;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            uint2 w;
-            w.x = pack_bf16x2(o[rt][dt][0] * inv, o[rt][dt][1] * inv);
-            w.y = pack_bf16x2(o[rt][dt][2] * inv, o[rt][dt][3] * inv);
-            *reinterpret_cast<uint2 *>(dst + dt * 16) = w;
-        }
-        if (lse != nullptr && q4 == 0)
-            lse[(size_t)row * H + g * G + head] = lt > 0.f ? (m[rt] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+    for (int dt = 0; dt < DT; ++dt) {
+        uint2 w;
+        w.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+        w.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+        *reinterpret_cast<uint2 *>(dst + dt * 16) = w;
     }
+    if (lse != nullptr && q4 == 0)
+        lse[(size_t)row * H + g * G + head] = lt > 0.f ? (m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int D, int RT, int NW>
+template <int D, int NW>
 hipError_t launch(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *ids,
                   float scale, uint16_t *out, float *lse, hipStream_t st) {
     const int G = s.H / s.h;
-    const int Tq = NW * RT * (16 / G);
+    const int Tq = NW * (16 / G);
     const int max_tiles = (s.max_q + Tq - 1) / Tq;
     const long grid = (long)max_tiles * s.num_seqs * s.h;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_prefill_tile<D, RT, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, q, k, v, ids,
-                       s.cu_q, s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL((attn_prefill_tile<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, q, k, v, ids, s.cu_q,
+                       s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, out, lse);
     return hipGetLastError();
 }
 
@@ -469,18 +523,20 @@ hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t
                                const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
     const int G = s.H / s.h;
     if (G < 1 || G > 16) return hipErrorInvalidValue;
-    // 8 waves; two row tiles per wave when the tile stays within 64 queries
-    // (one mask bit per query), else one; 4 waves of one tile for G = 1.
+    // One 16-row tile per wave, as many waves as keep the tile within 64
+    // queries (one mask bit per query), at most 16 (four per SIMD).
     const int qt = 16 / G;
+    const int cap = 64 / qt;
+    const int nw = cap >= 16 ? 16 : (cap >= 8 ? 8 : 4);
     if (s.d == 64) {
-        if (8 * 2 * qt <= 64) return launch<64, 2, 8>(s, q, k, v, ids, scale, out, lse, st);
-        if (8 * qt <= 64) return launch<64, 1, 8>(s, q, k, v, ids, scale, out, lse, st);
-        return launch<64, 1, 4>(s, q, k, v, ids, scale, out, lse, st);
+        if (nw == 16) return launch<64, 16>(s, q, k, v, ids, scale, out, lse, st);
+        if (nw == 8) return launch<64, 8>(s, q, k, v, ids, scale, out, lse, st);
+        return launch<64, 4>(s, q, k, v, ids, scale, out, lse, st);
     }
     if (s.d == 128) {
-        if (8 * 2 * qt <= 64) return launch<128, 2, 8>(s, q, k, v, ids, scale, out, lse, st);
-        if (8 * qt <= 64) return launch<128, 1, 8>(s, q, k, v, ids, scale, out, lse, st);
-        return launch<128, 1, 4>(s, q, k, v, ids, scale, out, lse, st);
+        if (nw == 16) return launch<128, 16>(s, q, k, v, ids, scale, out, lse, st);
+        if (nw == 8) return launch<128, 8>(s, q, k, v, ids, scale, out, lse, st);
+        return launch<128, 4>(s, q, k, v, ids, scale, out, lse, st);
     }
     return hipErrorInvalidValue;
 }

@@ -63,12 +63,15 @@ def compare_ids(oracle, inp, rows, gpu_ids, ref_ids, kth, tie):
 def assert_close(gpu, ref, what=""):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
-    err = np.abs(gpu - ref)
-    bound = ATOL + RTOL * np.abs(ref)
-    bad = err > bound
+    with np.errstate(invalid="ignore"):
+        err = np.abs(gpu - ref)
+        bound = ATOL + RTOL * np.abs(ref)
+        # equal values (infinities included) match; a NaN anywhere else is a mismatch
+        bad = ~((gpu == ref) | (err <= bound))
+    err = np.where(gpu == ref, 0.0, err)
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance; "
                              f"max err {err.max():.3g}; first bad {idx.tolist()} gpu "
                              f"{gpu[tuple(idx[0])]:.6g} ref {ref[tuple(idx[0])]:.6g}")
-    return float(err.max())
+    return float(np.nanmax(err)) if err.size else 0.0
