@@ -49,17 +49,39 @@ constexpr int kStages = 4;   // ring depth (sub-blocks)
 // Fourth word of a raw buffer resource (32-bit data format, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
 
+// Layout of one ring stage (a 64-token sub-block of K, then of V).
+//  * d = 128 ("grouped"): every 1 KB load instruction fills 4 whole token
+//    rows; groups of 4 rows sit GROUP = 1056 bytes apart.  16-token MFMA
+//    tile tt holds tokens 4m + tt (m = 0..15), i.e. row tt of every group, so
+//    lane m of a K operand read and the lanes of a transposing V read step
+//    through groups, 1056 = 32 (mod 256) bytes apart: bank-conflict free for
+//    both ds_read_b128 and ds_read_b64_tr_b16.
+//  * d = 64 ("padded"): rows padded to 2d+16 (K) and 2d+64 (V) bytes, tile
+//    tt holds tokens 16 tt .. 16 tt + 15; loads fill 16-byte slots in order.
 template <int D>
 struct Ring {
+    static constexpr bool GROUPED = (D == 128);
+    static constexpr int GROUP = 1056;
     static constexpr int KROW = D * 2 + 16;
     static constexpr int VROW = D * 2 + 64;
     static constexpr int KSLOT_ROW = KROW / 16;   // 16-byte slots per row
     static constexpr int VSLOT_ROW = VROW / 16;
     static constexpr int KINSTR = KSLOT_ROW;      // 64 rows x slots / 64 lanes per load
     static constexpr int VINSTR = VSLOT_ROW;
-    static constexpr int KBYTES = 64 * KROW;
-    static constexpr int VBYTES = 64 * VROW;
+    static constexpr int KBYTES = GROUPED ? 16 * GROUP : 64 * KROW;
+    static constexpr int VBYTES = GROUPED ? 16 * GROUP : 64 * VROW;
     static constexpr int STAGE = KBYTES + VBYTES;
+    // K operand reads: lane stride (MFMA row) and offset between 16-token tiles
+    static constexpr int K_LANE = GROUPED ? GROUP : KROW;
+    static constexpr int K_TILE = GROUPED ? 256 : 16 * KROW;
+    // transposing V reads: lane-group stride, tile 2 s2 + 1 offset, s2 offset
+    static constexpr int V_LANE = GROUPED ? GROUP : VROW;
+    static constexpr int V_ODD = GROUPED ? 256 : 16 * VROW;
+    static constexpr int V_S2 = GROUPED ? 512 : 32 * VROW;
+    // token (within the sub-block) of MFMA row 4 q4 + i of tile tt
+    static __device__ __forceinline__ int token(int tt, int q4, int i) {
+        return GROUPED ? 16 * q4 + 4 * i + tt : 16 * tt + 4 * q4 + i;
+    }
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
@@ -246,15 +268,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const uint32_t list_u0 = lds_addr(list_u), list_m0 = lds_addr(list_m), list_n0 = lds_addr(list_n);
     const uint32_t ready0 = lds_addr(ready), done0 = lds_addr(done);
     // Per-lane read offsets inside a stage.
-    const uint32_t k_rd = (uint32_t)(l16 * R::KROW + q4 * 16);
-    const uint32_t v_rd = (uint32_t)(R::KBYTES + (4 * q4 + (l16 >> 2)) * R::VROW + 8 * (l16 & 3));
+    const uint32_t k_rd = (uint32_t)(l16 * R::K_LANE + q4 * 16);
+    const uint32_t v_rd = (uint32_t)(R::KBYTES + (4 * q4 + (l16 >> 2)) * R::V_LANE + 8 * (l16 & 3));
 
     // Direct loads of one 64-token sub-block into a ring stage, all issued by
-    // one wave: lane i of load instruction n fills 16-byte slot 64n + i of the
-    // stage's K (then V) rows.  The loads go through a buffer resource that
-    // ends at the sequence's last token, so rows past it read as zeros (they
-    // are masked later) and pad slots, given an out-of-range offset, move no
-    // data at all.
+    // one wave (lane i of a load instruction writes 16 bytes at M0 + 16 i).
+    // The loads go through a buffer resource that ends at the group's row of
+    // the sequence's last token; rows past the end repeat that token (finite
+    // data, masked later), and pad slots of the padded layout, given an
+    // out-of-range offset, move no data at all.
     auto issue_all = [&](int t0_in, int stage_in) {
         const int t0 = __builtin_amdgcn_readfirstlane(t0_in);
         const int stage = __builtin_amdgcn_readfirstlane(stage_in);
@@ -267,31 +289,57 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
         // recomputed per call (kept out of registers across the loop)
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        {
-            int row = ln / R::KSLOT_ROW, c16 = ln % R::KSLOT_ROW;
+        if constexpr (R::GROUPED) {
+            // instruction n: rows 4n .. 4n + 3, lane -> row 4n + ln/16, chunk ln%16
+            if (t0 + 63 < len_k) {
+                int off = (ln >> 4) * hd2 + (ln & 15) * 16;
 #pragma unroll
-            for (int i = 0; i < R::KINSTR; ++i) {
-                const int off = c16 < CPR ? row * hd2 + c16 * 16 : 0x7fffffff;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(base + i * 1024), 16, off, 0, 0, 0);
-                row += 64 / R::KSLOT_ROW;
-                c16 += 64 % R::KSLOT_ROW;
-                if (c16 >= R::KSLOT_ROW) {
-                    c16 -= R::KSLOT_ROW;
-                    ++row;
+                for (int n = 0; n < 16; ++n) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(base + n * R::GROUP), 16, off, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(base + R::KBYTES + n * R::GROUP), 16, off,
+                                                             0, 0, 0);
+                    off += 4 * hd2;
+                }
+            } else {
+                // the sequence ends inside the sub-block: later rows repeat its last token
+                const int lim = len_k - 1 - t0;
+#pragma unroll
+                for (int n = 0; n < 16; ++n) {
+                    const int off = min(4 * n + (ln >> 4), lim) * hd2 + (ln & 15) * 16;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(base + n * R::GROUP), 16, off, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(base + R::KBYTES + n * R::GROUP), 16, off,
+                                                             0, 0, 0);
                 }
             }
-        }
-        {
-            int row = ln / R::VSLOT_ROW, c16 = ln % R::VSLOT_ROW;
+        } else {
+            const int lim = min(63, len_k - 1 - t0);
+            {
+                int row = ln / R::KSLOT_ROW, c16 = ln % R::KSLOT_ROW;
 #pragma unroll
-            for (int i = 0; i < R::VINSTR; ++i) {
-                const int off = c16 < CPR ? row * hd2 + c16 * 16 : 0x7fffffff;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(base + R::KBYTES + i * 1024), 16, off, 0, 0, 0);
-                row += 64 / R::VSLOT_ROW;
-                c16 += 64 % R::VSLOT_ROW;
-                if (c16 >= R::VSLOT_ROW) {
-                    c16 -= R::VSLOT_ROW;
-                    ++row;
+                for (int i = 0; i < R::KINSTR; ++i) {
+                    const int off = c16 < CPR ? min(row, lim) * hd2 + c16 * 16 : 0x7fffffff;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(base + i * 1024), 16, off, 0, 0, 0);
+                    row += 64 / R::KSLOT_ROW;
+                    c16 += 64 % R::KSLOT_ROW;
+                    if (c16 >= R::KSLOT_ROW) {
+                        c16 -= R::KSLOT_ROW;
+                        ++row;
+                    }
+                }
+            }
+            {
+                int row = ln / R::VSLOT_ROW, c16 = ln % R::VSLOT_ROW;
+#pragma unroll
+                for (int i = 0; i < R::VINSTR; ++i) {
+                    const int off = c16 < CPR ? min(row, lim) * hd2 + c16 * 16 : 0x7fffffff;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(base + R::KBYTES + i * 1024), 16, off, 0, 0,
+                                                             0);
+                    row += 64 / R::VSLOT_ROW;
+                    c16 += 64 % R::VSLOT_ROW;
+                    if (c16 >= R::VSLOT_ROW) {
+                        c16 -= R::VSLOT_ROW;
+                        ++row;
+                    }
                 }
             }
         }
@@ -305,7 +353,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
             uint4 a[2 * KS];
-            lds_k_pair<KS, 16 * R::KROW>(a, sbase + k_rd + tp * 32 * R::KROW);
+            lds_k_pair<KS, R::K_TILE>(a, sbase + k_rd + tp * 2 * R::K_TILE);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 sacc[2 * tp + u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -323,7 +371,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (t0 + tt * 16 + 4 * q4 + i > prow) sacc[tt][i] = -INFINITY;
+                    if (t0 + R::token(tt, q4, i) > prow) sacc[tt][i] = -INFINITY;
         }
         float mloc = -INFINITY;
 #pragma unroll
@@ -335,7 +383,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
         // than kLazy, so weights stay <= 2^kLazy and O is rarely rescaled.
         const bool move = selected && mloc > m_ref + kLazy;
         if (__ballot(move) != 0ull) {
-            const float alpha = move ? exp2f(m_ref - mloc) : 1.0f;   // 0 on a row's first block
+            const float alpha = move ? fast_exp2(m_ref - mloc) : 1.0f;   // 0 on a row's first block
             m_ref = move ? mloc : m_ref;
             l *= alpha;
 #pragma unroll
@@ -347,7 +395,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float e = exp2f(fmaf(sacc[tt][i], c2, -bias));
+                const float e = fast_exp2(fmaf(sacc[tt][i], c2, -bias));
                 sacc[tt][i] = e;
                 lsum += e;
             }
@@ -367,7 +415,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
 #pragma unroll
             for (int dq = 0; dq < DT / 4; ++dq) {
                 i16x4 va[4], vb[4];
-                lds_v_half<4, 16 * R::VROW>(va, vb, sbase + v_rd + s2 * 32 * R::VROW + dq * 128);
+                lds_v_half<4, R::V_ODD>(va, vb, sbase + v_rd + s2 * R::V_S2 + dq * 128);
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const bf16x8 vop = as_bf16x8(pack_tr(va[x], vb[x]));

@@ -70,6 +70,11 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // Reductions with the lane 16 (resp. 32) positions away: the swap returns the
 // own value in one slot and the partner's in the other.
+// 2^x with the hardware v_exp_f32: results below 2^-126 come out as zero
+// (softmax weights that small relative to the row maximum are negligible),
+// without the denormal range fix-up exp2f adds around it.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float max_xor16(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

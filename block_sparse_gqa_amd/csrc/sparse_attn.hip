@@ -141,14 +141,14 @@ __device__ __forceinline__ void softmax_sub(Acc<D> &acc, f32x4 (&s)[kTT], int le
     mloc = max_xor32(max_xor16(mloc));
     const float m_new = fmaxf(acc.m, mloc);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2f(acc.m - m_use);
+    const float alpha = fast_exp2(acc.m - m_use);
     acc.m = m_new;
     float lsum = 0.0f;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e = exp2f(s[tt][i] - m_use);
+            const float e = fast_exp2(s[tt][i] - m_use);
             s[tt][i] = e;
             lsum += e;
         }
