@@ -206,13 +206,14 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
-    int num_seqs, int H, int h, int B, int top_k, int max_tiles, float c2, uint16_t *__restrict__ out,
-    float *__restrict__ lse) {
+    int num_seqs, int H, int h, int B, int top_k, int max_tiles, float c2, const int *__restrict__ v_exp,
+    uint16_t *__restrict__ out, float *__restrict__ lse) {
     using R = Ring<D>;
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
     constexpr int CPR = D / 8;   // data slots per row
     constexpr float kLazy = 8.0f;   // log2 headroom before the reference max moves
+    constexpr float kPScale = 7.0f; // weights are taken as 2^7 p (<= 2^15, fp16 normal down to 2^-21 p)
     __shared__ __attribute__((aligned(16))) char ring[kStages * R::STAGE];
     __shared__ unsigned long long masks[kWin];
     __shared__ unsigned long long list_m[kWin];
@@ -389,39 +390,32 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
         }
-        const float bias = (selected && m_ref > -INFINITY) ? m_ref : INFINITY;
+        const float nbias = (selected && m_ref > -INFINITY) ? kPScale - m_ref : -INFINITY;
         float lsum = 0.0f;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float e = fast_exp2(fmaf(sacc[tt][i], c2, -bias));
+                const float e = fast_exp2(fmaf(sacc[tt][i], c2, nbias));
                 sacc[tt][i] = e;
                 lsum += e;
             }
         l += lsum;
-        // O^T += V^T . P^T, P split into a bf16 head and tail
+        // O^T += V^T . P^T in fp16 (V is the scaled fp16 copy)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             // slots 8*q4 + i <- tile 2*s2 value i, slots 8*q4 + 4 + i <- tile 2*s2+1 value i
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                hi[i] = split_bf16x2(sacc[2 * s2][2 * i], sacc[2 * s2][2 * i + 1], &lo[i]);
-                hi[2 + i] = split_bf16x2(sacc[2 * s2 + 1][2 * i], sacc[2 * s2 + 1][2 * i + 1], &lo[2 + i]);
-            }
-            const bf16x8 p_hi = as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]});
-            const bf16x8 p_lo = as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]});
+            const f16x8 p16 = as_f16x8(uint4{pack_f16x2(sacc[2 * s2][0], sacc[2 * s2][1]),
+                                             pack_f16x2(sacc[2 * s2][2], sacc[2 * s2][3]),
+                                             pack_f16x2(sacc[2 * s2 + 1][0], sacc[2 * s2 + 1][1]),
+                                             pack_f16x2(sacc[2 * s2 + 1][2], sacc[2 * s2 + 1][3])});
 #pragma unroll
             for (int dq = 0; dq < DT / 4; ++dq) {
                 i16x4 va[4], vb[4];
                 lds_v_half<4, R::V_ODD>(va, vb, sbase + v_rd + s2 * R::V_S2 + dq * 128);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const bf16x8 vop = as_bf16x8(pack_tr(va[x], vb[x]));
-                    o[4 * dq + x] = mfma16x16x32(vop, p_hi, o[4 * dq + x]);
-                    o[4 * dq + x] = mfma16x16x32(vop, p_lo, o[4 * dq + x]);
-                }
+                for (int x = 0; x < 4; ++x)
+                    o[4 * dq + x] = mfma16x16x32_f16(as_f16x8(pack_tr(va[x], vb[x])), p16, o[4 * dq + x]);
             }
         }
     };
@@ -539,7 +533,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const float lt = sum_xor32(sum_xor16(l));
     if (prow < 0) return;
     const int row = q_begin + r0 + qidx;
-    const float inv = lt > 0.f ? 1.0f / lt : 0.0f;
+    const float inv = lt > 0.f ? __builtin_ldexpf(1.0f / lt, *v_exp) : 0.0f;
     uint16_t *dst = out + ((size_t)row * H + g * G + head) * D + 4 * q4;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -549,44 +543,128 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
         *reinterpret_cast<uint2 *>(dst + dt * 16) = w;
     }
     if (lse != nullptr && q4 == 0)
-        lse[(size_t)row * H + g * G + head] = lt > 0.f ? (m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+        lse[(size_t)row * H + g * G + head] =
+            lt > 0.f ? (m_ref - kPScale + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+}
+
+// fp16 copy of V for the P.V products.  Every value is scaled by the same
+// power of two 2^-e, chosen from max |V| so that the largest lands in
+// [2^14, 2^15): bf16 values within 2^25 of the largest convert exactly, and
+// smaller ones lose only bits below 2^-10 of the largest.  The output is
+// multiplied back by 2^e.
+constexpr int kCvtParts = 1024;   // workgroups of the max pass
+
+__global__ __launch_bounds__(256) void v_absmax_bits(const uint4 *__restrict__ v, long n16,
+                                                     uint32_t *__restrict__ part) {
+    uint32_t m = 0;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256) {
+        const uint4 x = v[i];
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+    }
+    // |bf16| bit patterns order like the values (NaN above infinity)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    __shared__ uint32_t red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float mul) {
+    return pack_f16x2(__uint_as_float(w << 16) * mul, __uint_as_float(w & 0xffff0000u) * mul);
+}
+
+__global__ __launch_bounds__(256) void v_to_f16(const uint4 *__restrict__ v, long n16,
+                                                const uint32_t *__restrict__ part, int nparts,
+                                                uint4 *__restrict__ v16, int *__restrict__ v_exp) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, part[i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    __shared__ uint32_t red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    // max |v| < 2^(E - 126) for bf16 exponent field E: scaling by 2^-(E - 141)
+    // puts it in [2^14, 2^15) whatever its magnitude (2^-e stays a normal
+    // float).  Infinities and NaN keep e = 0 and pass through as such.
+    const int e = (m >= 0x7f80u) ? 0 : max(-126, (int)(m >> 7) - 141);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *v_exp = e;
+    const float mul = __builtin_ldexpf(1.0f, -e);
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256) {
+        const uint4 x = v[i];
+        v16[i] = uint4{bf16x2_to_f16x2(x.x, mul), bf16x2_to_f16x2(x.y, mul), bf16x2_to_f16x2(x.z, mul),
+                       bf16x2_to_f16x2(x.w, mul)};
+    }
+}
+
+struct PrefillWs {
+    size_t v16_off, part_off, exp_off, bytes;
+};
+PrefillWs prefill_ws(const Shape &s) {
+    PrefillWs w;
+    const size_t vb = (size_t)s.total_k * s.h * s.d * 2;
+    w.v16_off = 0;
+    w.part_off = (vb + 255) / 256 * 256;
+    w.exp_off = w.part_off + kCvtParts * sizeof(uint32_t);
+    w.bytes = w.exp_off + 256;
+    return w;
 }
 
 template <int D, int NW>
-hipError_t launch(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *ids,
-                  float scale, uint16_t *out, float *lse, hipStream_t st) {
+hipError_t launch(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v16, const int *v_exp,
+                  const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
     const int G = s.H / s.h;
     const int Tq = NW * (16 / G);
     const int max_tiles = (s.max_q + Tq - 1) / Tq;
     const long grid = (long)max_tiles * s.num_seqs * s.h;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_prefill_tile<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, q, k, v, ids, s.cu_q,
-                       s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL((attn_prefill_tile<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, q, k, v16, ids, s.cu_q,
+                       s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, v_exp, out, lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t prefill_workspace_bytes(const Shape &s) { return prefill_ws(s).bytes; }
+
 hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                               const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
+                               const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
+                               hipStream_t st) {
     const int G = s.H / s.h;
     if (G < 1 || G > 16) return hipErrorInvalidValue;
+    if (s.d != 64 && s.d != 128) return hipErrorInvalidValue;
+    if (s.total_k < 1) return hipErrorInvalidValue;
+    // fp16 copy of V (two small passes over V)
+    const PrefillWs w = prefill_ws(s);
+    char *wsb = static_cast<char *>(ws);
+    uint16_t *v16 = reinterpret_cast<uint16_t *>(wsb + w.v16_off);
+    uint32_t *part = reinterpret_cast<uint32_t *>(wsb + w.part_off);
+    int *v_exp = reinterpret_cast<int *>(wsb + w.exp_off);
+    const long n16 = (long)s.total_k * s.h * s.d / 8;
+    const long need = (n16 + 255) / 256;
+    const int nparts = (int)(need < kCvtParts ? need : kCvtParts);
+    hipLaunchKernelGGL(v_absmax_bits, dim3(nparts), dim3(256), 0, st, reinterpret_cast<const uint4 *>(v), n16, part);
+    const int ncvt = (int)(need < 4096 ? need : 4096);
+    hipLaunchKernelGGL(v_to_f16, dim3(ncvt), dim3(256), 0, st, reinterpret_cast<const uint4 *>(v), n16, part, nparts,
+                       reinterpret_cast<uint4 *>(v16), v_exp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     // One 16-row tile per wave, as many waves as keep the tile within 64
     // queries (one mask bit per query), at most 16 (four per SIMD).
     const int qt = 16 / G;
     const int cap = 64 / qt;
     const int nw = cap >= 16 ? 16 : (cap >= 8 ? 8 : 4);
     if (s.d == 64) {
-        if (nw == 16) return launch<64, 16>(s, q, k, v, ids, scale, out, lse, st);
-        if (nw == 8) return launch<64, 8>(s, q, k, v, ids, scale, out, lse, st);
-        return launch<64, 4>(s, q, k, v, ids, scale, out, lse, st);
+        if (nw == 16) return launch<64, 16>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
+        if (nw == 8) return launch<64, 8>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
+        return launch<64, 4>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
     }
-    if (s.d == 128) {
-        if (nw == 16) return launch<128, 16>(s, q, k, v, ids, scale, out, lse, st);
-        if (nw == 8) return launch<128, 8>(s, q, k, v, ids, scale, out, lse, st);
-        return launch<128, 4>(s, q, k, v, ids, scale, out, lse, st);
-    }
-    return hipErrorInvalidValue;
+    if (nw == 16) return launch<128, 16>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
+    if (nw == 8) return launch<128, 8>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
+    return launch<128, 4>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
 }
 
 }  // namespace msa

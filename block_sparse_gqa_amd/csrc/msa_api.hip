@@ -102,7 +102,7 @@ size_t msa_workspace_size(int op, const msa_problem_t *problem) {
             return index_ws(p);
         case MSA_OP_SPARSE_ATTN_PREFILL:
             if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
-            return 0;
+            return msa::prefill_workspace_bytes(to_shape(p));
         case MSA_OP_SPARSE_ATTN_DECODE:
             if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
             if (p.max_seqlen_q != 1 || p.total_q != p.num_seqs) return (size_t)-1;
@@ -133,8 +133,6 @@ msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf1
                                      const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
                                      msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
                                      msa_stream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     msa_status_t st = check_problem(problem);
     if (st != MSA_SUCCESS) return st;
     const msa_problem_t &p = *problem;
@@ -144,7 +142,8 @@ msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf1
     if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
     if ((st = attn_support(p)) != MSA_SUCCESS) return st;
     Shape s = to_shape(p);
-    return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse,
+    if ((st = check_ws(workspace, workspace_bytes, msa::prefill_workspace_bytes(s))) != MSA_SUCCESS) return st;
+    return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 

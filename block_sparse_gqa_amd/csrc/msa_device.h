@@ -43,6 +43,15 @@ __device__ __forceinline__ uint32_t split_bf16x2(float x0, float x1, uint32_t *l
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+// Two floats -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
 __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 // 16-byte global load that yields zeros when `ok` is false.  The load itself
@@ -61,6 +70,11 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same shape with fp16 operands.
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // D(32x32, f32) += A(32x16) * B(16x32).  Operand layout (lane l, q = l / 32):
 //   A: row l % 32, k = 8q .. 8q+7;  B: column l % 32, k = 8q .. 8q+7;
 //   D[i] (i < 16): column l % 32, row 8*(i/4) + 4q + (i%4).
@@ -68,13 +82,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Reductions with the lane 16 (resp. 32) positions away: the swap returns the
-// own value in one slot and the partner's in the other.
 // 2^x with the hardware v_exp_f32: results below 2^-126 come out as zero
 // (softmax weights that small relative to the row maximum are negligible),
 // without the denormal range fix-up exp2f adds around it.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions with the lane 16 (resp. 32) positions away: the swap returns the
+// own value in one slot and the partner's in the other.
 __device__ __forceinline__ float max_xor16(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

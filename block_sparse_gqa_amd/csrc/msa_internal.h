@@ -29,8 +29,10 @@ hipError_t launch_topk_select(const Shape &s, const float *scores, int32_t *ids,
 int max_select_blocks();
 
 // Sparse branch.
+size_t prefill_workspace_bytes(const Shape &s);
 hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                               const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st);
+                               const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
+                               hipStream_t st);
 int decode_splits(const Shape &s);
 size_t decode_workspace_bytes(const Shape &s);
 hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,

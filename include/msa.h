@@ -121,7 +121,10 @@ msa_status_t msa_index_topk(const msa_problem_t *problem, const msa_bf16_t *q_id
  * out      [total_q, H, d] bf16 (written)
  * lse      [total_q, H] float32 natural-log sum-exp of the scaled logits
  *          (written), or NULL
- * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_PREFILL) bytes.
+ * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_PREFILL) bytes,
+ *          16-byte aligned: an fp16 copy of v (every value scaled by one
+ *          power of two that puts max |v| in [2^14, 2^15), undone on the
+ *          output) used for the P.V products, plus a few KB.
  */
 msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf16_t *q,
                                      const msa_bf16_t *k, const msa_bf16_t *v,

@@ -61,7 +61,10 @@ def test_workspace_size(lib):
     p = prob()
     # [total_q, h, round_up(ceil(max_k / B), 4)] float32 block scores
     assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p)) == 128 * 2 * 4 * 4
-    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == 0
+    # fp16 copy of V [total_k, h, d] (256-byte aligned) + 1024 partial maxima + the scale exponent
+    vbytes = p.total_k * p.num_kv_heads * p.head_dim * 2
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == \
+        (vbytes + 255) // 256 * 256 + 1024 * 4 + 256
     # decode needs max_seqlen_q == 1
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_DECODE, ctypes.byref(p)) == msa.SIZE_MAX
     d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)
@@ -110,6 +113,10 @@ def test_attention_rejects(lib):
     assert attn_call(lib, pre, prob(), out=None) == msa.MSA_ERROR_INVALID_VALUE
     assert attn_call(lib, pre, prob(), scale=0.0) == msa.MSA_ERROR_INVALID_VALUE
     assert attn_call(lib, pre, prob(), scale=float("nan")) == msa.MSA_ERROR_INVALID_VALUE
+    # prefill needs its workspace (the fp16 copy of V)
+    need = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(prob()))
+    assert attn_call(lib, pre, prob(), ws=None) == msa.MSA_ERROR_WORKSPACE
+    assert attn_call(lib, pre, prob(), ws=FAKE, ws_bytes=need - 1) == msa.MSA_ERROR_WORKSPACE
     # decode demands one query per sequence
     assert attn_call(lib, dec, prob()) == msa.MSA_ERROR_INVALID_VALUE
     d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)

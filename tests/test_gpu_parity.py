@@ -97,6 +97,29 @@ def test_small_cases(case):
     check_case(inp, label=name)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("log2_scale", [24, -24])
+def test_value_magnitude(log2_scale):
+    """V scaled by 2^24 and 2^-24 (exactly, in bf16): O scales by the same
+    power of two, so O / 2^s must meet the tolerance against the oracle's
+    O / 2^s (the tolerance is stated for unit-scale values).  The prefill
+    path's fp16 copy of V is rescaled by a power of two internally, which must
+    be invisible."""
+    from block_sparse_gqa_amd import device
+    inp = synth.custom((600, 129), (600, 129), 8, 2, 128, 64, 64, 4, seed=11, name=f"v_2^{log2_scale}")
+    f = np.float32(2.0 ** log2_scale)
+    inp.v[...] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.v) * f)
+    rows = np.arange(inp.wl.total_q, dtype=np.int64)
+    ref_ids, _, _ = oracle.index_topk(inp, rows)
+    ref_out, ref_lse = oracle.sparse_attention(inp, ref_ids, rows)
+    dp = device.upload(inp)
+    out, lse = device.sparse_attention(dp, torch.from_numpy(ref_ids).to(dp.q.device))
+    torch.cuda.synchronize()
+    err = parity.assert_close(out.float().cpu().numpy() / f, ref_out / f, f"{inp.wl.name} attention / 2^s")
+    parity.assert_close(lse.cpu().numpy(), ref_lse, f"{inp.wl.name} lse")
+    say(f"[{inp.wl.name}] max err of O / 2^s: {err:.3g}")
+
+
 def test_dense_equivalence_through_gpu():
     """k >= #blocks: the GPU output equals dense causal attention; here the
     oracle (itself pinned to float64 dense attention) is the reference and the
