@@ -14,6 +14,8 @@
 // plus one permlane32 swap.  K_idx tiles are double-buffered in LDS; the
 // block scores of 16 consecutive blocks are staged in LDS and written to the
 // [row, group, block] workspace as contiguous runs.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -26,7 +28,7 @@ constexpr int kCols = 64;     // columns per wave
 constexpr int kStage = 16;    // blocks per staged flush
 
 template <int DI, int B>
-__global__ __launch_bounds__(256) void index_prefill_blockmax(
+__global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int h,
     float *__restrict__ scores, int e_stride) {
@@ -96,7 +98,10 @@ __global__ __launch_bounds__(256) void index_prefill_blockmax(
     lstore(0);
     __syncthreads();
 
-    for (int j = 0; j < nblk; ++j) {
+    // One key block: scores on MFMA, Block Max Pool, staged flush.  MASK is
+    // needed only on the diagonal blocks, where some key follows some column.
+    auto step = [&](int j, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = j & 1;
         if (j + 1 < nblk) gload(j + 1);
 
@@ -122,7 +127,6 @@ __global__ __launch_bounds__(256) void index_prefill_blockmax(
         }
 
         // Block Max Pool: keys after a column's position are not visible.
-        const bool need_mask = j * B + B - 1 > p_first;
         const int slot = j % kStage;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void index_prefill_blockmax(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     float v = acc[mt][nt][i];
-                    if (need_mask) {
+                    if constexpr (MASK) {
                         const int t = j * B + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                         if (t > col_p[nt]) v = -INFINITY;
                     }
@@ -166,7 +170,12 @@ __global__ __launch_bounds__(256) void index_prefill_blockmax(
 
         if (j + 1 < nblk) lstore(buf ^ 1);
         __syncthreads();
-    }
+    };
+    // blocks [0, j_full) are entirely visible to every column of the tile
+    const int j_full = min(nblk, (p_first + 1) / B);
+    int j = 0;
+    for (; j < j_full; ++j) step(j, std::false_type{});
+    for (; j < nblk; ++j) step(j, std::true_type{});
 }
 
 template <int DI, int B>
