@@ -117,6 +117,14 @@ __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict_
 #pragma unroll
         for (int v = 0; v < VPT; ++v) c += __builtin_popcountll(__ballot(key[v] >= cand));
         if (c >= k) T = cand;
+        if (c == k) {
+            // exactly k keys are >= cand: they are the selection (the k-th and
+            // (k+1)-th largest keys are on opposite sides of cand, so no tie
+            // crosses the boundary); lowering T to cand - 1 keeps every one of
+            // them "> T" below
+            T = cand - 1u;
+            break;
+        }
     }
     int n_gt = 0, n_eq = 0;
 #pragma unroll
@@ -179,6 +187,7 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
     __shared__ int hist[kBins];
     __shared__ int red[kNW];
     __shared__ uint32_t bc[4];
+    __shared__ int exact;
 
     const long pair = blockIdx.x;
     const int t = threadIdx.x;
@@ -206,6 +215,7 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
     if (t == 0) {
         bc[0] = 0u;
         bc[1] = 0xffffffffu;
+        exact = 0;
     }
     __syncthreads();
     if ((t & 63) == 0) {
@@ -242,15 +252,24 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
             if (b0 >= 0 && above < rank && above + c0 >= rank) {
                 bc[2] = (uint32_t)b0;
                 bc[3] = (uint32_t)above;
+                exact = (above + c0 == rank) ? 1 : 0;
             } else if (b1 >= 0 && above + c0 < rank && above + c0 + c1 >= rank) {
                 bc[2] = (uint32_t)b1;
                 bc[3] = (uint32_t)(above + c0);
+                exact = (above + c0 + c1 == rank) ? 1 : 0;
             }
             __syncthreads();
             P |= bc[2] << sh;
             rank -= (int)bc[3];
             lo_bit = sh;
+            const bool done = exact != 0;
             __syncthreads();
+            if (done && P > 0u) {
+                // the k-th largest key is the smallest in its bin: the keys
+                // from that bin up are exactly the selection, no tie crosses it
+                P -= 1u;
+                break;
+            }
         }
         T = P;
     }
@@ -304,6 +323,7 @@ int max_select_blocks() { return kNT * 64; }
 hipError_t launch_topk_select(const Shape &s, const float *scores, int32_t *ids, hipStream_t st) {
     const int e = score_stride(s);
     if (e <= 64 * 4) return launch_wave<4>(s, scores, ids, st);
+    if (e <= 64 * 8) return launch_wave<8>(s, scores, ids, st);
     if (e <= 64 * 16) return launch_wave<16>(s, scores, ids, st);
     if (e <= 64 * 32) return launch_wave<32>(s, scores, ids, st);
     if (e <= kNT * 16) return launch_block<16>(s, scores, ids, st);
