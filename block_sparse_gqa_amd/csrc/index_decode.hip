@@ -8,7 +8,7 @@
 // takes the i-th 16-byte chunk of a contiguous 1 KB run): instructions that
 // touch half lines stream markedly slower on this part.  The block is then
 // re-laid out through a padded per-wave LDS tile into the MFMA operand
-// layout.  The next block of the wave is already in flight in registers while
+// layout.  The wave's next two blocks are already in flight in registers while
 // the current one is scored; blocks are dealt round-robin over the waves.
 //
 // Scores.  Tokens run along the M dimension of v_mfma_f32_16x16x32_bf16 and
@@ -59,31 +59,27 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     for (int ks = 0; ks < KS; ++ks)
         qop[ks] = as_bf16x8(load16_if(q_idx + ((size_t)row * h + g) * DI + 32 * ks + 8 * q4, g < h, q_idx));
 
-    auto load_block = [&](uint4 (&r)[T::LOADS], int j) {
+    // Plain loads (no select on the loaded values, so nothing waits for them
+    // until the block is used); rows past the sequence end repeat its last
+    // key and are masked below.
+    auto load_block = [&](uint4(&r)[T::LOADS], int j) {
         const int t0 = j * B;
-        const uint16_t *base = k_idx + (size_t)(k_begin + t0) * DI;
-        const bool inside = t0 + B <= len_k;
 #pragma unroll
         for (int x = 0; x < T::LOADS; ++x) {
             const int ci = x * 64 + lane;
             const int tok = ci / T::CPR, c16 = ci % T::CPR;
-            if (inside) r[x] = load16(base + tok * DI + c16 * 8);
-            else r[x] = load16_if(base + tok * DI + c16 * 8, t0 + tok < len_k, k_idx);
+            const int t = min(t0 + tok, len_k - 1);
+            r[x] = load16(k_idx + (size_t)(k_begin + t) * DI + c16 * 8);
         }
     };
 
-    uint4 cur[T::LOADS], nxt[T::LOADS];
-    int j = j_first;
-    if (j < E) load_block(cur, j);
-    for (; j < E; j += nwaves) {
-        const bool more = j + nwaves < E;
-        if (more) load_block(nxt, j + nwaves);
-        // registers -> LDS (token-major, padded rows)
+    // One block: registers -> padded LDS tile -> MFMA -> Block Max Pool.
+    auto score_block = [&](const uint4(&r)[T::LOADS], int j) {
 #pragma unroll
         for (int x = 0; x < T::LOADS; ++x) {
             const int ci = x * 64 + lane;
             const int tok = ci / T::CPR, c16 = ci % T::CPR;
-            *reinterpret_cast<uint4 *>(my + tok * T::ROW + c16 * 16) = cur[x];
+            *reinterpret_cast<uint4 *>(my + tok * T::ROW + c16 * 16) = r[x];
         }
         wave_lds_sync();
         float m = -INFINITY;
@@ -106,10 +102,29 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
         m = max_xor16(m);
         m = max_xor32(m);
         if (lane < h) scores[((size_t)row * h + lane) * e_stride + j] = m;
-        if (more) {
-#pragma unroll
-            for (int x = 0; x < T::LOADS; ++x) cur[x] = nxt[x];
-        }
+    };
+
+    // Three register sets rotate so that two blocks are in flight while one
+    // is scored; the loop is unrolled by three to keep the sets static.
+    // Loads are issued unconditionally (past the wave's last block they
+    // repeat it, a cache hit), so the wait before each block covers exactly
+    // that block's loads and never the two younger ones.
+    if (j_first >= E) return;
+    const int j_last = j_first + (E - 1 - j_first) / nwaves * nwaves;
+    uint4 ra[T::LOADS], rb[T::LOADS], rc[T::LOADS];
+    int j = j_first;
+    load_block(ra, j);
+    load_block(rb, min(j + nwaves, j_last));
+    for (;; j += 3 * nwaves) {
+        load_block(rc, min(j + 2 * nwaves, j_last));
+        score_block(ra, j);
+        if (j + nwaves > j_last) break;
+        load_block(ra, min(j + 3 * nwaves, j_last));
+        score_block(rb, j + nwaves);
+        if (j + 2 * nwaves > j_last) break;
+        load_block(rb, min(j + 4 * nwaves, j_last));
+        score_block(rc, j + 2 * nwaves);
+        if (j + 3 * nwaves > j_last) break;
     }
 }
 

@@ -73,24 +73,27 @@ __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
         for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = as_bf16x8(load16_if(src + 16 * ks, ok, q_idx));
     }
 
+    // Tile prefetch: plain loads (no select on the loaded value, which would
+    // make the wave wait for them right away); rows past the sequence end
+    // repeat its last key and are masked with the diagonal blocks.
+    // CHUNKS is a multiple of 256 for every supported (d_idx, B).
+    static_assert(CHUNKS % 256 == 0, "tile chunks must fill whole passes");
     uint4 pre[PASSES];
     auto gload = [&](int j) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int ci = ps * 256 + tid;
             const int row = ci / CPR, c8 = ci % CPR;
-            const int t = j * B + row;
-            pre[ps] = load16_if(k_idx + (size_t)(k_begin + t) * DI + c8 * 8, ci < CHUNKS && t < len_k, k_idx);
+            const int t = min(j * B + row, len_k - 1);
+            pre[ps] = load16(k_idx + (size_t)(k_begin + t) * DI + c8 * 8);
         }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int ci = ps * 256 + tid;
-            if (ci < CHUNKS) {
-                const int row = ci / CPR, c8 = ci % CPR;
-                *reinterpret_cast<uint4 *>(&ktile[buf][row * ROWB + c8 * 16]) = pre[ps];
-            }
+            const int row = ci / CPR, c8 = ci % CPR;
+            *reinterpret_cast<uint4 *>(&ktile[buf][row * ROWB + c8 * 16]) = pre[ps];
         }
     };
 
