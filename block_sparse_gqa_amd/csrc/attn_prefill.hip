@@ -46,6 +46,8 @@ typedef __attribute__((address_space(1))) void gbl_void;
 
 constexpr int kWin = 256;    // key blocks per union window (one per thread)
 constexpr int kStages = 4;   // ring depth (sub-blocks)
+// Upper bound on polls of one ready stamp (each poll sleeps ~64 cycles).
+constexpr int kSpinLimit = 1 << 20;
 // Fourth word of a raw buffer resource (32-bit data format, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -474,10 +476,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
         // published after its next item, or before it would block, so no wave
         // ever waits while holding an unpublished stage.  Waves skip items
         // they have no work in and run ahead until the ring holds them back.
+        // initial fill of every stage, spread over the waves
         if (wave < kStages && wave < nitems) {
-            issue_all(t0_of(wave), wave);
+            for (int x = wave; x < kStages && x < nitems; x += NW) issue_all(t0_of(x), x);
             wait_vm<0>();
-            lds_store_u32(ready0 + 4 * wave, wave + 1);
+            for (int x = wave; x < kStages && x < nitems; x += NW) lds_store_u32(ready0 + 4 * x, x + 1);
         }
         int pend_stage = -1, pend_stamp = 0;
         auto publish = [&]() {
@@ -504,8 +507,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
                     const int t0 = blk * B + sub * 64;
                     if (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) != it + 1) {
                         publish();
-                        while (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) != it + 1)
+                        // bounded (kSpinLimit polls, tens of milliseconds, far above any
+                        // real wait): a broken protocol would end the kernel with wrong
+                        // results instead of hanging the device
+                        for (int spin = 0; spin < kSpinLimit; ++spin) {
+                            if (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) == it + 1) break;
                             __builtin_amdgcn_s_sleep(1);
+                        }
                     }
                     const uint32_t sbase = ring0 + stage * R::STAGE;
                     if (t0 <= p_wave_last) {
