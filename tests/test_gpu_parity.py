@@ -167,6 +167,28 @@ def test_determinism():
     np.testing.assert_array_equal(a["out"], b["out"])
 
 
+# name, seqlens_q, seqlens_k, H, h, d, d_idx, B, k: selection paths the headline
+# workloads do not reach.
+LONG = [
+    # 32768 blocks: workgroup select with 32 keys per thread; top_k at its maximum
+    ("decode_e32k_k4096", (1, 1), (2_097_152, 1_500_000), 4, 1, 64, 32, 64, 4096),
+    # 62500 blocks: 64 keys per thread
+    ("decode_e62k", (1,), (4_000_000,), 2, 1, 64, 32, 64, 64),
+    # 1250 blocks: one wave per row with 32 keys per lane
+    ("prefill_e1250", (80_000,), (80_000,), 4, 2, 64, 32, 64, 8),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", LONG, ids=[c[0] for c in LONG])
+def test_long_rows(case):
+    name, sq, sk, H, h, d, di, B, k = case
+    inp = synth.custom(sq, sk, H, h, d, di, B, k, seed=zlib.crc32(name.encode()) % 1000, name=name)
+    rows = None if inp.wl.is_decode else synth.sample_rows(inp.wl, n_per_seq=96)
+    rep, _ = check_case(inp, rows=rows, label=name)
+    say(f"[{name}] near-tie pairs {rep['near_tie']} of {rep['pairs']}, in-band flips {rep['band_flips']}")
+
+
 _CACHE = {}
 
 
