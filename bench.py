@@ -132,6 +132,53 @@ def measured_traffic(kernel_file, symbol, launches_per_call):
     return None
 
 
+def paged_decode(inp, dp, ids_contig, contig, steps, warmup):
+    """The same decode step over a paged copy of the cache: pages scattered
+    at random through a pool with spare pages, filled by the append kernel.
+    Reported beside the headline (which uses the contiguous cache)."""
+    import torch
+
+    from block_sparse_gqa_amd import device
+    wl = inp.wl
+    blocks = sum((n + wl.block_size - 1) // wl.block_size for n in wl.seqlens_k)
+    num_pages = blocks + blocks // 16
+    table = device.random_page_table(wl.seqlens_k, wl.block_size, num_pages, seed=17)
+    pc = device.alloc_paged(wl, table, num_pages)
+    log(f"[bench] paged copy of {wl.name}: {blocks} blocks in a pool of {num_pages} pages")
+    slots = device.cache_slots(dp, table)
+    device.page_in(dp, pc, table, slots)   # once untimed (the same rows are written again below)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    device.page_in(dp, pc, table, slots)
+    e[1].record()
+    torch.cuda.synchronize()
+    t_append = e[0].elapsed_time(e[1])
+    append_bytes = 2 * wl.total_k * (2 * wl.num_kv_heads * wl.head_dim + wl.index_dim) * 2   # read + write
+    ids = device.alloc_ids(dp)
+    out, lse = device.alloc_out(dp)
+    for _ in range(warmup):
+        device.index_topk_paged(dp, pc, ids)
+        device.sparse_attention_paged(dp, pc, ids, out, lse)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for x in ev:
+        x[0].record()
+        device.index_topk_paged(dp, pc, ids)
+        x[1].record()
+        device.sparse_attention_paged(dp, pc, ids, out, lse)
+        x[2].record()
+    torch.cuda.synchronize()
+    t_idx = float(np.mean([x[0].elapsed_time(x[1]) for x in ev]))
+    t_att = float(np.mean([x[1].elapsed_time(x[2]) for x in ev]))
+    gbs = contig["algorithmic_GB"] / ((t_idx + t_att) * 1e-3)
+    same = bool(torch.equal(ids, ids_contig))
+    del pc
+    torch.cuda.empty_cache()
+    return {"ms": t_idx + t_att, "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "GB_per_s": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "pages": num_pages, "ids_equal_contiguous": same,
+            "page_in_ms": t_append, "page_in_GB_per_s": append_bytes / (t_append * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +186,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workloads", default=",".join(WORKLOADS))
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-cache decode measurement (reported beside the headline, not in it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -243,6 +292,12 @@ def main():
     roofline = {"bound": kbound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": measured_traffic(*ksrc) if ksrc else None,
                 "traffic_unit": "bytes per launch", "avg_launch_ms": kms}
+
+    if not args.no_paged:
+        for name in names:
+            if inputs[name].wl.is_decode:
+                results[name]["paged"] = paged_decode(inputs[name], dps[name], bufs[name][0], results[name],
+                                                      max(args.steps, 5), args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:

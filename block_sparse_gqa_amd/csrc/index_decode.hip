@@ -31,11 +31,14 @@ struct IdxTile {
     static constexpr int LOADS = B * CPR / 64;       // 16-byte loads per lane per block
 };
 
-template <int DI, int B>
+// PAGED: k_idx is a pool of pages of B rows and block j of sequence s sits in
+// page table[s * table_stride + j] (clamped into [0, num_pages)).
+template <int DI, int B, bool PAGED>
 __global__ __launch_bounds__(256) void index_decode_blockmax(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int h,
-    float *__restrict__ scores, int e_stride) {
+    float *__restrict__ scores, int e_stride, const int32_t *__restrict__ table, int table_stride,
+    int num_pages) {
     using T = IdxTile<DI, B>;
     constexpr int KS = DI / 32;   // 32-dim k-steps
     constexpr int TT = B / 16;    // 16-token tiles per block
@@ -63,13 +66,20 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     // until the block is used); rows past the sequence end repeat its last
     // key and are masked below.
     auto load_block = [&](uint4(&r)[T::LOADS], int j) {
+        j = __builtin_amdgcn_readfirstlane(j);
         const int t0 = j * B;
+        // pool row of the block's first token
+        size_t row0 = (size_t)(k_begin + t0);
+        if constexpr (PAGED) {
+            const int pg = min(max(table[(size_t)s * table_stride + j], 0), num_pages - 1);
+            row0 = (size_t)pg * B;
+        }
 #pragma unroll
         for (int x = 0; x < T::LOADS; ++x) {
             const int ci = x * 64 + lane;
             const int tok = ci / T::CPR, c16 = ci % T::CPR;
-            const int t = min(t0 + tok, len_k - 1);
-            r[x] = load16(k_idx + (size_t)(k_begin + t) * DI + c16 * 8);
+            const int t = min(tok, len_k - 1 - t0);
+            r[x] = load16(k_idx + (row0 + t) * DI + c16 * 8);
         }
     };
 
@@ -136,8 +146,12 @@ hipError_t launch(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx, 
     const int need = (e_max + kWaves - 1) / kWaves;
     if (per_seq > need) per_seq = need;
     dim3 grid(per_seq, s.num_seqs);
-    hipLaunchKernelGGL((index_decode_blockmax<DI, B>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q, s.cu_k, s.h,
-                       scores, score_stride(s));
+    if (s.table != nullptr)
+        hipLaunchKernelGGL((index_decode_blockmax<DI, B, true>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q, s.cu_k,
+                           s.h, scores, score_stride(s), s.table, s.table_stride, s.num_pages);
+    else
+        hipLaunchKernelGGL((index_decode_blockmax<DI, B, false>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q,
+                           s.cu_k, s.h, scores, score_stride(s), nullptr, 0, 0);
     return hipGetLastError();
 }
 

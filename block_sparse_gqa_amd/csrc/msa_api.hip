@@ -166,4 +166,82 @@ msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// The paged entry points: decode only, a table and a pool of at least one page.
+msa_status_t check_paged(const msa_problem_t &p, const msa_paged_kv_t *pk) {
+    if (pk == nullptr || pk->block_table == nullptr || pk->num_pages < 1) return MSA_ERROR_INVALID_VALUE;
+    const long blocks = ((long)p.max_seqlen_k + p.block_size - 1) / p.block_size;
+    if (pk->max_blocks_per_seq < blocks) return MSA_ERROR_INVALID_VALUE;
+    if (p.max_seqlen_q != 1 || p.total_q != p.num_seqs) return MSA_ERROR_NOT_SUPPORTED;
+    return MSA_SUCCESS;
+}
+
+void set_paged(Shape &s, const msa_paged_kv_t &pk) {
+    s.table = pk.block_table;
+    s.table_stride = pk.max_blocks_per_seq;
+    s.num_pages = pk.num_pages;
+}
+
+}  // namespace
+
+msa_status_t msa_index_topk_paged(const msa_problem_t *problem, const msa_paged_kv_t *paged, const msa_bf16_t *q_idx,
+                                  const msa_bf16_t *k_idx_pool, int32_t *topk_ids, void *workspace,
+                                  size_t workspace_bytes, msa_stream_t stream) {
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if ((st = check_paged(p, paged)) != MSA_SUCCESS) return st;
+    if (q_idx == nullptr || k_idx_pool == nullptr || topk_ids == nullptr) return MSA_ERROR_INVALID_VALUE;
+    if ((st = index_support(p)) != MSA_SUCCESS) return st;
+    if ((st = check_ws(workspace, workspace_bytes, index_ws(p))) != MSA_SUCCESS) return st;
+    Shape s = to_shape(p);
+    set_paged(s, *paged);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    float *scores = reinterpret_cast<float *>(workspace);
+    if (msa::launch_index_decode(s, q_idx, k_idx_pool, scores, hs) != hipSuccess) return MSA_ERROR_LAUNCH;
+    return launched(msa::launch_topk_select(s, scores, topk_ids, hs));
+}
+
+msa_status_t msa_sparse_attn_decode_paged(const msa_problem_t *problem, const msa_paged_kv_t *paged,
+                                          const msa_bf16_t *q, const msa_bf16_t *k_pool, const msa_bf16_t *v_pool,
+                                          const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out, float *lse,
+                                          void *workspace, size_t workspace_bytes, msa_stream_t stream) {
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if ((st = check_paged(p, paged)) != MSA_SUCCESS) return st;
+    if (q == nullptr || k_pool == nullptr || v_pool == nullptr || topk_ids == nullptr || out == nullptr)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
+    if ((st = attn_support(p)) != MSA_SUCCESS) return st;
+    Shape s = to_shape(p);
+    if ((st = check_ws(workspace, workspace_bytes, msa::decode_workspace_bytes(s))) != MSA_SUCCESS) return st;
+    set_paged(s, *paged);
+    return launched(msa::launch_attn_decode(s, q, k_pool, v_pool, topk_ids, softmax_scale, out, lse, workspace,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+msa_status_t msa_kv_append_paged(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t index_dim,
+                                 int64_t pool_rows, const int32_t *slot_mapping, const msa_bf16_t *k,
+                                 const msa_bf16_t *v, const msa_bf16_t *k_idx, msa_bf16_t *k_pool,
+                                 msa_bf16_t *v_pool, msa_bf16_t *k_idx_pool, msa_stream_t stream) {
+    if (num_tokens < 0 || pool_rows < 1 || num_kv_heads < 1) return MSA_ERROR_INVALID_VALUE;
+    if (head_dim != 64 && head_dim != 128) return MSA_ERROR_NOT_SUPPORTED;
+    if (index_dim != 32 && index_dim != 64) return MSA_ERROR_NOT_SUPPORTED;
+    if (num_kv_heads > 64) return MSA_ERROR_NOT_SUPPORTED;
+    if (num_tokens == 0) return MSA_SUCCESS;
+    if (slot_mapping == nullptr || k == nullptr || v == nullptr || k_idx == nullptr || k_pool == nullptr ||
+        v_pool == nullptr || k_idx_pool == nullptr)
+        return MSA_ERROR_INVALID_VALUE;
+    const void *ptrs[] = {k, v, k_idx, k_pool, v_pool, k_idx_pool};
+    for (const void *q : ptrs)
+        if ((reinterpret_cast<uintptr_t>(q) & 15u) != 0) return MSA_ERROR_INVALID_VALUE;
+    return launched(msa::launch_kv_append(num_tokens, num_kv_heads, head_dim, index_dim, (long long)pool_rows,
+                                          slot_mapping, k, v, k_idx, k_pool, v_pool, k_idx_pool,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

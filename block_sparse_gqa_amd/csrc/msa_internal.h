@@ -11,6 +11,10 @@ struct Shape {
     int num_seqs, total_q, total_k, max_q, max_k;
     int H, h, d, d_idx, B, top_k;
     const int32_t *cu_q, *cu_k;
+    // Paged cache (decode only): page of logical block j of sequence s is
+    // table[s * table_stride + j]; null table = contiguous packed cache.
+    const int32_t *table = nullptr;
+    int table_stride = 0, num_pages = 0;
 };
 
 // Block-level scores workspace: [total_q, h, e_stride] float32.
@@ -33,6 +37,10 @@ size_t prefill_workspace_bytes(const Shape &s);
 hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                hipStream_t st);
+// Copy new K/V/K_idx rows into paged pools at the given pool rows.
+hipError_t launch_kv_append(int n, int h, int d, int d_idx, long long pool_rows, const int32_t *slots,
+                            const uint16_t *k, const uint16_t *v, const uint16_t *k_idx, uint16_t *k_pool,
+                            uint16_t *v_pool, uint16_t *k_idx_pool, hipStream_t st);
 int decode_splits(const Shape &s);
 size_t decode_workspace_bytes(const Shape &s);
 hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,

@@ -63,17 +63,19 @@ __device__ __forceinline__ float head_total(float l) {
 // K and V rows of one sub-block.  Every load instruction reads whole lines
 // (lane i takes the i-th 16-byte chunk of 4 consecutive 256-byte rows), which
 // streams markedly faster than operand-shaped loads; rows are re-laid out
-// through LDS.  t0 is wave-uniform: the base address is scalar and lanes add
-// 32-bit offsets.  Tokens past the sequence end read as zeros.
+// through LDS.  row0 (the cache row of the sub-block's first token) and nvalid
+// (its tokens before the sequence end) are wave-uniform: the base address is
+// scalar and lanes add 32-bit offsets.  Tokens past the end read as zeros.
 template <int D>
 __device__ __forceinline__ void load_kv(uint4 (&kr)[DecodeLds<D>::CH], uint4 (&vr)[DecodeLds<D>::CH],
-                                        const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, size_t k_begin,
-                                        int len_k, int t0, int h, int g) {
+                                        const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int row0_in,
+                                        int nvalid_in, int h, int g) {
     constexpr int CPR = D / 8;
     const int lane = lane_id();
-    t0 = __builtin_amdgcn_readfirstlane(t0);
-    const size_t base = ((k_begin + t0) * h + g) * D;
-    const bool inside = t0 + kSub <= len_k;
+    const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
+    const int nvalid = __builtin_amdgcn_readfirstlane(nvalid_in);
+    const size_t base = ((size_t)row0 * h + g) * D;
+    const bool inside = nvalid >= kSub;
 #pragma unroll
     for (int x = 0; x < DecodeLds<D>::CH; ++x) {
         const int ci = x * 64 + lane;
@@ -83,8 +85,8 @@ __device__ __forceinline__ void load_kv(uint4 (&kr)[DecodeLds<D>::CH], uint4 (&v
             kr[x] = load16(k + base + off);
             vr[x] = load16(v + base + off);
         } else {
-            kr[x] = load16_if(k + base + off, t0 + tok < len_k, k);
-            vr[x] = load16_if(v + base + off, t0 + tok < len_k, v);
+            kr[x] = load16_if(k + base + off, tok < nvalid, k);
+            vr[x] = load16_if(v + base + off, tok < nvalid, v);
         }
     }
 }
@@ -195,16 +197,20 @@ __device__ __forceinline__ void pv_half(Acc<D> &acc, const f32x4 (&s)[kTT], cons
 // One wave per (split, group, sequence): attend its share of the selected
 // blocks; write the partial output (normalised) and its log2-sum-exp.
 // The current sub-block sits in LDS while the next one's loads are in flight.
-template <int D, int B>
+// PAGED: k and v are pools of pages of B rows; block j of sequence s sits in
+// page table[s * table_stride + j] (clamped into [0, num_pages)).
+template <int D, int B, bool PAGED>
 __global__ __launch_bounds__(64, 2) void attn_decode_split(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
-    int H, int h, int top_k, int per_split, float c2, float *__restrict__ part_o, float *__restrict__ part_lse) {
+    int H, int h, int top_k, int per_split, float c2, float *__restrict__ part_o, float *__restrict__ part_lse,
+    const int32_t *__restrict__ table, int table_stride, int num_pages) {
     using L = DecodeLds<D>;
     constexpr int NSUB = B / kSub;
     __shared__ __attribute__((aligned(16))) char klds[L::KBYTES];
     __shared__ __attribute__((aligned(16))) char vlds[L::VBYTES];
-    __shared__ int list[kChunk * NSUB];
+    __shared__ int list[kChunk * NSUB];   // first token of each sub-block (sequence position)
+    __shared__ int rows[kChunk * NSUB];   // its cache row
     const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int nsplit = gridDim.x;
     const int G = H / h;
@@ -232,21 +238,27 @@ __global__ __launch_bounds__(64, 2) void attn_decode_split(
         // Sub-block starts of this chunk's valid, causal ids (any id order).
         const int a = c0 + lane;
         const int j = a < a1 ? sel[a] : -1;
+        const bool jok = j >= 0 && j <= p / B;
+        int row_j = (int)k_begin + j * B;
+        if constexpr (PAGED) row_j = jok ? min(max(table[(size_t)s * table_stride + j], 0), num_pages - 1) * B : 0;
         int n = 0;
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
-            const bool ok = j >= 0 && j <= p / B && j * B + sb * kSub <= p;
+            const bool ok = jok && j * B + sb * kSub <= p;
             const unsigned long long bal = __ballot(ok);
             const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-            if (ok) list[n + pos] = j * B + sb * kSub;
+            if (ok) {
+                list[n + pos] = j * B + sb * kSub;
+                rows[n + pos] = row_j + sb * kSub;
+            }
             n += __builtin_popcountll(bal);
         }
         wave_lds_sync();
         if (n == 0) continue;
-        load_kv<D>(kA, vA, k, v, k_begin, len_k, list[0], h, g);
-        if (n > 1) load_kv<D>(kB, vB, k, v, k_begin, len_k, list[1], h, g);
+        load_kv<D>(kA, vA, k, v, rows[0], len_k - list[0], h, g);
+        if (n > 1) load_kv<D>(kB, vB, k, v, rows[1], len_k - list[1], h, g);
         store_kv<D>(kA, vA, klds, vlds);
-        if (n > 2) load_kv<D>(kA, vA, k, v, k_begin, len_k, list[2], h, g);
+        if (n > 2) load_kv<D>(kA, vA, k, v, rows[2], len_k - list[2], h, g);
         for (int i = 0; i < n; i += 2) {
             // sub-block i in LDS; set B holds i+1, set A holds i+2
             wave_lds_sync();
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_split(
             wave_lds_sync();
             if (i + 1 >= n) break;
             store_kv<D>(kB, vB, klds, vlds);
-            if (i + 3 < n) load_kv<D>(kB, vB, k, v, k_begin, len_k, list[i + 3], h, g);
+            if (i + 3 < n) load_kv<D>(kB, vB, k, v, rows[i + 3], len_k - list[i + 3], h, g);
             // sub-block i+1 in LDS; set A holds i+2, set B holds i+3
             wave_lds_sync();
             qk_sub<D>(sc, klds, qop);
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_split(
             wave_lds_sync();
             if (i + 2 >= n) break;
             store_kv<D>(kA, vA, klds, vlds);
-            if (i + 4 < n) load_kv<D>(kA, vA, k, v, k_begin, len_k, list[i + 4], h, g);
+            if (i + 4 < n) load_kv<D>(kA, vA, k, v, rows[i + 4], len_k - list[i + 4], h, g);
         }
     }
     const float l = head_total(acc.l);
@@ -346,8 +358,13 @@ hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, c
     const int per = (s.top_k + nsplit - 1) / nsplit;
     float *part_o = reinterpret_cast<float *>(ws);
     float *part_lse = part_o + (size_t)s.num_seqs * s.H * nsplit * s.d;
-    hipLaunchKernelGGL((attn_decode_split<D, B>), dim3(nsplit, s.h, s.num_seqs), dim3(64), 0, st, q, k, v, ids,
-                       s.cu_q, s.cu_k, s.H, s.h, s.top_k, per, scale * kLog2e, part_o, part_lse);
+    const dim3 grid(nsplit, s.h, s.num_seqs);
+    if (s.table != nullptr)
+        hipLaunchKernelGGL((attn_decode_split<D, B, true>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.H,
+                           s.h, s.top_k, per, scale * kLog2e, part_o, part_lse, s.table, s.table_stride, s.num_pages);
+    else
+        hipLaunchKernelGGL((attn_decode_split<D, B, false>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.H,
+                           s.h, s.top_k, per, scale * kLog2e, part_o, part_lse, nullptr, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_decode_merge<D>), dim3(s.H, s.num_seqs), dim3(64), 0, st, part_o, part_lse, s.H, nsplit,

@@ -86,3 +86,87 @@ def forward(dp: DeviceProblem, ids=None, out=None, lse=None, stream=None):
     ids = index_topk(dp, ids, stream)
     out, lse = sparse_attention(dp, ids, out, lse, stream)
     return ids, out, lse
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache (decode): pools of pages of B token rows plus a block table.
+
+
+@dataclass
+class PagedCache:
+    table: torch.Tensor        # [num_seqs, max_blocks_per_seq] int32 page ids (device)
+    num_pages: int
+    k_pool: torch.Tensor       # [num_pages * B, h, d] bf16
+    v_pool: torch.Tensor       # [num_pages * B, h, d] bf16
+    k_idx_pool: torch.Tensor   # [num_pages * B, d_idx] bf16
+    paged: msa.msa_paged_kv_t
+
+
+def random_page_table(seqlens_k, block_size: int, num_pages: int, seed: int = 0) -> np.ndarray:
+    """Host block table giving every logical block of every sequence a distinct
+    page, drawn at random from num_pages (>= the total number of blocks)."""
+    blocks = [(n + block_size - 1) // block_size for n in seqlens_k]
+    if sum(blocks) > num_pages:
+        raise ValueError("pool too small for the sequences")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pages = rng.permutation(num_pages)[: sum(blocks)].astype(np.int32)
+    table = np.full((len(blocks), max(blocks)), -1, np.int32)
+    at = 0
+    for s, nb in enumerate(blocks):
+        table[s, :nb] = pages[at: at + nb]
+        at += nb
+    return table
+
+
+def slot_mapping(table: np.ndarray, seq: np.ndarray, pos: np.ndarray, block_size: int) -> np.ndarray:
+    """Pool row of token `pos` of sequence `seq` (vectors of equal length)."""
+    return (table[seq, pos // block_size].astype(np.int64) * block_size + pos % block_size).astype(np.int32)
+
+
+def alloc_paged(wl, table: np.ndarray, num_pages: int, device="cuda", fill_seed: int = 7) -> PagedCache:
+    """Pools of num_pages pages filled with finite noise (so a wrong page read
+    shows up), and the block table on the device."""
+    g = torch.Generator(device=device)
+    g.manual_seed(fill_seed)
+    rows = num_pages * wl.block_size
+
+    def noise(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+    t = torch.from_numpy(np.ascontiguousarray(table, np.int32)).to(device)
+    return PagedCache(t, num_pages, noise(rows, wl.num_kv_heads, wl.head_dim), noise(rows, wl.num_kv_heads, wl.head_dim),
+                      noise(rows, wl.index_dim), msa.make_paged(t, num_pages))
+
+
+def append(pc: PagedCache, slots: torch.Tensor, k, v, k_idx, stream=None):
+    msa.msa_kv_append_paged(slots, k, v, k_idx, pc.k_pool, pc.v_pool, pc.k_idx_pool, stream)
+
+
+def cache_slots(dp: DeviceProblem, table: np.ndarray) -> torch.Tensor:
+    """Pool rows of every token of a contiguous problem's cache, in packed order."""
+    wl = dp.wl
+    seq = np.repeat(np.arange(len(wl.seqlens_k)), wl.seqlens_k)
+    pos = np.concatenate([np.arange(n) for n in wl.seqlens_k])
+    return torch.from_numpy(slot_mapping(table, seq, pos, wl.block_size)).to(dp.k.device)
+
+
+def page_in(dp: DeviceProblem, pc: PagedCache, table: np.ndarray, slots=None, stream=None):
+    """Copy a contiguous problem's whole cache into the pools (one append of every token)."""
+    if slots is None:
+        slots = cache_slots(dp, table)
+    append(pc, slots, dp.k, dp.v, dp.k_idx, stream)
+
+
+def index_topk_paged(dp: DeviceProblem, pc: PagedCache, ids=None, stream=None) -> torch.Tensor:
+    if ids is None:
+        ids = alloc_ids(dp)
+    msa.msa_index_topk_paged(dp.problem, pc.paged, dp.q_idx, pc.k_idx_pool, ids, dp.ws_index, stream)
+    return ids
+
+
+def sparse_attention_paged(dp: DeviceProblem, pc: PagedCache, ids, out=None, lse=None, stream=None):
+    if out is None:
+        out, lse = alloc_out(dp)
+    msa.msa_sparse_attn_decode_paged(dp.problem, pc.paged, dp.q, pc.k_pool, pc.v_pool, ids, dp.wl.scale, out, lse,
+                                     dp.ws_attn, stream)
+    return out, lse

@@ -52,6 +52,14 @@ class msa_problem_t(ctypes.Structure):
     ]
 
 
+class msa_paged_kv_t(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -71,6 +79,14 @@ def load():
     lib.msa_sparse_attn_prefill.restype = ctypes.c_int
     lib.msa_sparse_attn_decode.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
     lib.msa_sparse_attn_decode.restype = ctypes.c_int
+    paged = ctypes.POINTER(msa_paged_kv_t)
+    lib.msa_index_topk_paged.argtypes = [prob, paged, P, P, P, P, S, P]
+    lib.msa_index_topk_paged.restype = ctypes.c_int
+    lib.msa_sparse_attn_decode_paged.argtypes = [prob, paged, P, P, P, P, ctypes.c_float, P, P, P, S, P]
+    lib.msa_sparse_attn_decode_paged.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.msa_kv_append_paged.argtypes = [i32, i32, i32, i32, ctypes.c_int64, P, P, P, P, P, P, P, P]
+    lib.msa_kv_append_paged.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [ctypes.c_int, prob]
     lib.msa_workspace_size.restype = S
     lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -157,3 +173,34 @@ def msa_sparse_attn_decode(problem, q, k_cache, v_cache, topk_ids, softmax_scale
                                          _ptr(topk_ids), float(softmax_scale), _ptr(out), _ptr(lse),
                                          _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "msa_sparse_attn_decode")
+
+
+def make_paged(block_table, num_pages) -> msa_paged_kv_t:
+    """block_table: device int32 tensor [num_seqs, max_blocks_per_seq] of page ids."""
+    pk = msa_paged_kv_t()
+    pk.block_table = _ptr(block_table)
+    pk.max_blocks_per_seq = int(block_table.shape[1])
+    pk.num_pages = int(num_pages)
+    return pk
+
+
+def msa_index_topk_paged(problem, paged, q_idx, k_idx_pool, topk_ids, workspace=None, stream=None):
+    _check(load().msa_index_topk_paged(ctypes.byref(problem), ctypes.byref(paged), _ptr(q_idx), _ptr(k_idx_pool),
+                                       _ptr(topk_ids), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "msa_index_topk_paged")
+
+
+def msa_sparse_attn_decode_paged(problem, paged, q, k_pool, v_pool, topk_ids, softmax_scale, out, lse=None,
+                                 workspace=None, stream=None):
+    _check(load().msa_sparse_attn_decode_paged(ctypes.byref(problem), ctypes.byref(paged), _ptr(q), _ptr(k_pool),
+                                               _ptr(v_pool), _ptr(topk_ids), float(softmax_scale), _ptr(out),
+                                               _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "msa_sparse_attn_decode_paged")
+
+
+def msa_kv_append_paged(slot_mapping, k, v, k_idx, k_pool, v_pool, k_idx_pool, stream=None):
+    """k, v [n, h, d], k_idx [n, d_idx]; pools [rows, h, d] / [rows, d_idx]; slot_mapping int32 [n]."""
+    n, h, d = (int(x) for x in k.shape)
+    _check(load().msa_kv_append_paged(n, h, d, int(k_idx.shape[1]), int(k_pool.shape[0]), _ptr(slot_mapping),
+                                      _ptr(k), _ptr(v), _ptr(k_idx), _ptr(k_pool), _ptr(v_pool), _ptr(k_idx_pool),
+                                      _stream(stream)), "msa_kv_append_paged")

@@ -150,6 +150,62 @@ msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16
                                     float *lse, void *workspace, size_t workspace_bytes,
                                     msa_stream_t stream);
 
+/*
+ * Paged KV cache (decode).  The pages keep the cache in the native GQA
+ * layout, one physical block of B tokens per page with the K/V slices of
+ * every group, and the index branch only picks which blocks to read
+ * ("深度解析M3多模态模型与Token Plan", section 二.1 on storage/compute
+ * decoupling: GQA physical blocks in a cache pool; "MiniMax M3 MSA vs Step
+ * 3.7 Flash MFA", section on the three deliberate subtractions: with GQA the
+ * serving engines' caches are reused unchanged).  Only the addressing
+ * differs from the contiguous entry points; the arithmetic is the same, so
+ * a paged call returns exactly what the contiguous call returns on the same
+ * logical cache.
+ *
+ * Pools (device, caller-owned):
+ *     k_pool, v_pool  [num_pages * B, h, d]     k_idx_pool  [num_pages * B, d_idx]
+ * Page i holds pool rows i*B .. i*B + B - 1.  Token t of sequence s lives in
+ * pool row block_table[s * max_blocks_per_seq + t / B] * B + t % B, where
+ * len(s) = cu_seqlens_k[s+1] - cu_seqlens_k[s] (cu_seqlens_k then only gives
+ * the lengths; total_k is their sum).  Page ids outside [0, num_pages) are
+ * clamped into it, which keeps every access inside the pools (the result is
+ * then meaningless, never a fault).  Several sequences may share a page
+ * (e.g. a common prefix).
+ */
+typedef struct {
+    const int32_t *block_table; /* device, [num_seqs, max_blocks_per_seq] page ids */
+    int32_t max_blocks_per_seq; /* row stride of block_table, >= ceil(max_seqlen_k / B) */
+    int32_t num_pages;          /* pages in each pool, >= 1 */
+} msa_paged_kv_t;
+
+/* msa_index_topk for decode (max_seqlen_q == 1, total_q == num_seqs) over a
+ * paged index-key cache.  Same workspace as msa_index_topk
+ * (msa_workspace_size(MSA_OP_INDEX_TOPK, problem)).  Other shapes return
+ * MSA_ERROR_NOT_SUPPORTED. */
+msa_status_t msa_index_topk_paged(const msa_problem_t *problem, const msa_paged_kv_t *paged,
+                                  const msa_bf16_t *q_idx, const msa_bf16_t *k_idx_pool, int32_t *topk_ids,
+                                  void *workspace, size_t workspace_bytes, msa_stream_t stream);
+
+/* msa_sparse_attn_decode over paged K/V pools.  Same workspace as
+ * msa_sparse_attn_decode (msa_workspace_size(MSA_OP_SPARSE_ATTN_DECODE,
+ * problem)). */
+msa_status_t msa_sparse_attn_decode_paged(const msa_problem_t *problem, const msa_paged_kv_t *paged,
+                                          const msa_bf16_t *q, const msa_bf16_t *k_pool, const msa_bf16_t *v_pool,
+                                          const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out, float *lse,
+                                          void *workspace, size_t workspace_bytes, msa_stream_t stream);
+
+/* Append: copy num_tokens new rows of k, v [num_tokens, h, d] and k_idx
+ * [num_tokens, d_idx] (device, bf16) into the pools at pool row
+ * slot_mapping[i] (device int32; the caller derives it from its block table
+ * as page * B + offset).  Slots < 0 are skipped (padding); slots >= pool_rows
+ * are skipped too, so a bad slot never writes outside the pools.  Rows with
+ * equal slots race (the caller's contract).  d in {64, 128}; d_idx in
+ * {32, 64}; 1 <= h <= 64.  No workspace. */
+msa_status_t msa_kv_append_paged(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t index_dim,
+                                 int64_t pool_rows, const int32_t *slot_mapping, const msa_bf16_t *k,
+                                 const msa_bf16_t *v, const msa_bf16_t *k_idx, msa_bf16_t *k_pool,
+                                 msa_bf16_t *v_pool, msa_bf16_t *k_idx_pool, msa_stream_t stream);
+
 /* Workspace bytes an entry point needs for `problem` (0 if none).  Returns
  * (size_t)-1 when the problem is invalid or unsupported for that op. */
 size_t msa_workspace_size(int op, const msa_problem_t *problem);

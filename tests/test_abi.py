@@ -121,3 +121,59 @@ def test_attention_rejects(lib):
     assert attn_call(lib, dec, prob()) == msa.MSA_ERROR_INVALID_VALUE
     d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)
     assert attn_call(lib, dec, d, ws=None) == msa.MSA_ERROR_WORKSPACE
+
+
+def paged(table=FAKE, stride=4, pages=16):
+    pk = msa.msa_paged_kv_t()
+    pk.block_table, pk.max_blocks_per_seq, pk.num_pages = table, stride, pages
+    return pk
+
+
+def dec_prob(**kw):
+    base = dict(num_seqs=2, total_q=2, cu_seqlens_q=FAKE, max_seqlen_q=1, total_k=400, max_seqlen_k=200)
+    base.update(kw)
+    return prob(**base)
+
+
+def test_paged_rejects(lib):
+    idx, att = lib.msa_index_topk_paged, lib.msa_sparse_attn_decode_paged
+    p = dec_prob()
+    need = lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p))
+
+    def icall(p, pk, q_idx=FAKE, ws=FAKE, ws_bytes=need):
+        return idx(ctypes.byref(p), ctypes.byref(pk) if pk is not None else None, q_idx, FAKE, FAKE, ws, ws_bytes,
+                   None)
+
+    assert icall(p, None) == msa.MSA_ERROR_INVALID_VALUE
+    assert icall(p, paged(table=None)) == msa.MSA_ERROR_INVALID_VALUE
+    assert icall(p, paged(pages=0)) == msa.MSA_ERROR_INVALID_VALUE
+    assert icall(p, paged(stride=3)) == msa.MSA_ERROR_INVALID_VALUE   # 200 tokens need 4 blocks of 64
+    assert icall(prob(), paged(stride=4)) == msa.MSA_ERROR_NOT_SUPPORTED   # prefill shapes are not paged
+    assert icall(p, paged(), q_idx=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert icall(p, paged(), ws_bytes=need - 1) == msa.MSA_ERROR_WORKSPACE
+
+    def acall(p, pk, q=FAKE, scale=0.088, ws=None, ws_bytes=0):
+        return att(ctypes.byref(p), ctypes.byref(pk), q, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE, None, ws,
+                   ws_bytes, None)
+
+    assert acall(p, paged(table=None)) == msa.MSA_ERROR_INVALID_VALUE
+    assert acall(p, paged(), q=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert acall(p, paged(), scale=-1.0) == msa.MSA_ERROR_INVALID_VALUE
+    assert acall(p, paged(), ws=None) == msa.MSA_ERROR_WORKSPACE
+    assert acall(dec_prob(head_dim=96), paged()) == msa.MSA_ERROR_NOT_SUPPORTED
+
+
+def test_append_rejects(lib):
+    app = lib.msa_kv_append_paged
+
+    def call(n=4, h=8, d=128, di=64, rows=1024, slots=FAKE, k=FAKE):
+        return app(n, h, d, di, rows, slots, k, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+
+    assert call(n=-1) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(rows=0) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(d=96) == msa.MSA_ERROR_NOT_SUPPORTED
+    assert call(di=48) == msa.MSA_ERROR_NOT_SUPPORTED
+    assert call(h=65) == msa.MSA_ERROR_NOT_SUPPORTED
+    assert call(slots=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(k=FAKE + 8) == msa.MSA_ERROR_INVALID_VALUE   # rows must be 16-byte aligned
+    assert call(n=0, slots=None, k=None) == msa.MSA_SUCCESS   # nothing to do
