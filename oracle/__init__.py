@@ -43,6 +43,9 @@ def _load():
         i32, i64 = ctypes.c_int, ctypes.c_int64
         lib.msa_oracle_index_topk.argtypes = [i32, P, P, i32, i32, i32, i32, P, P, i64, P, P, P, P, i32]
         lib.msa_oracle_index_topk.restype = i32
+        lib.msa_oracle_index_topk_forced.argtypes = [i32, P, P, i32, i32, i32, i32, i32, i32, P, P, i64, P, P, P,
+                                                     P, i32]
+        lib.msa_oracle_index_topk_forced.restype = i32
         lib.msa_oracle_block_scores.argtypes = [i32, P, P, i32, i32, i32, P, P, i64, i32, P, i64]
         lib.msa_oracle_block_scores.restype = i64
         lib.msa_oracle_sparse_attention.argtypes = [i32, P, P, i32, i32, i32, i32, i32, P, P, P, P,
@@ -66,11 +69,13 @@ def _rows(inp, rows):
     return _c(rows, np.int64)
 
 
-def index_topk(inp, rows=None, threads: int = 0):
+def index_topk(inp, rows=None, threads: int = 0, sink: int = 0, local: int = 0):
     """Oracle index branch for the given packed query rows (default: all).
 
     ``inp`` carries cu_seqlens_q/k, q_idx, k_idx (bf16 bits) and ``wl`` with
-    num_kv_heads, index_dim, block_size, top_k.
+    num_kv_heads, index_dim, block_size, top_k.  ``sink`` / ``local`` force
+    the first / the last (diagonal-ending) blocks into every selection
+    (0, 0 = plain TopK; sink + local <= top_k).
     Returns (ids [n, h, k] int32, kth [n, h, 2] float32, near_tie [n, h] bool).
     """
     wl = inp.wl
@@ -81,9 +86,9 @@ def index_topk(inp, rows=None, threads: int = 0):
     tie = np.empty((n, h), np.uint8)
     cu_q, cu_k = _c(inp.cu_seqlens_q, np.int32), _c(inp.cu_seqlens_k, np.int32)
     qi, ki = _c(inp.q_idx, np.uint16), _c(inp.k_idx, np.uint16)
-    rc = _load().msa_oracle_index_topk(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), h, wl.index_dim,
-                                       wl.block_size, k, _ptr(qi), _ptr(ki), n, _ptr(rows),
-                                       _ptr(ids), _ptr(kth), _ptr(tie), threads)
+    rc = _load().msa_oracle_index_topk_forced(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), h, wl.index_dim,
+                                              wl.block_size, k, int(sink), int(local), _ptr(qi), _ptr(ki), n,
+                                              _ptr(rows), _ptr(ids), _ptr(kth), _ptr(tie), threads)
     if rc != 0:
         raise ValueError("oracle index_topk rejected its input")
     return ids, kth, tie.astype(bool)

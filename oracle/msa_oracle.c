@@ -143,20 +143,42 @@ static int by_id(const void *a, const void *b)
 }
 
 /* TopK per (query, group) [P4 MSA section; P5 section 1: TopK decides which
- * KV blocks this layer and this GQA group keep].  Returns 0 or -1. */
-static int topk_blocks(const float *S, int64_t E, int top_k, int32_t *ids, float *kth, uint8_t *near_tie)
+ * KV blocks this layer and this GQA group keep].
+ *
+ * Optional forced inclusion (not part of the pages' method, which is pure
+ * TopK; an option for the attention-sink and local-window blocks that [P5]
+ * section 2 and [P4] section "waiting for the technical report" speculate
+ * may stand in for the dropped sliding-window branch): blocks 0..sink-1 and
+ * the `local` blocks ending at the diagonal block E-1 are always kept, and
+ * the other min(k, E) - |forced| slots go to the remaining blocks in the
+ * same (score descending, id ascending) order.  sink = local = 0 is plain
+ * TopK.  Needs sink + local <= top_k.  Returns 0 or -1. */
+static int topk_blocks(const float *S, int64_t E, int top_k, int sink, int local, int32_t *ids, float *kth,
+                       uint8_t *near_tie)
 {
+    if (sink < 0 || local < 0 || sink + local > top_k) return -1;
     cand_t *c = (cand_t *)malloc((size_t)E * sizeof(cand_t));
     if (!c) return -1;
-    for (int64_t j = 0; j < E; ++j) { c[j].score = S[j]; c[j].block = (int32_t)j; }
-    qsort(c, (size_t)E, sizeof(cand_t), by_score_then_id);
     int64_t m = E < top_k ? E : top_k;
-    for (int64_t i = 0; i < m; ++i) ids[i] = c[i].block;
+    int64_t nf = 0, nr = 0;   /* forced blocks (straight into ids), ranked rest (into c) */
+    for (int64_t j = 0; j < E; ++j) {
+        if (j < sink || j >= E - local) {
+            ids[nf++] = (int32_t)j;
+        } else {
+            c[nr].score = S[j];
+            c[nr].block = (int32_t)j;
+            ++nr;
+        }
+    }
+    qsort(c, (size_t)nr, sizeof(cand_t), by_score_then_id);
+    int64_t take = m - nf;   /* >= 0: nf <= min(sink + local, E) <= m */
+    for (int64_t i = 0; i < take; ++i) ids[nf + i] = c[i].block;
     qsort(ids, (size_t)m, sizeof(int32_t), by_id);
     for (int64_t i = m; i < top_k; ++i) ids[i] = -1;
-    /* near-tie: the k-th and (k+1)-th scores differ by <= 1e-3 relative */
-    if (E > top_k) {
-        float a = c[top_k - 1].score, b = c[top_k].score;
+    /* near-tie: the last kept and the first dropped ranked scores differ by
+     * <= 1e-3 relative (with nothing forced: the k-th and (k+1)-th scores) */
+    if (take > 0 && nr > take) {
+        float a = c[take - 1].score, b = c[take].score;
         kth[0] = a;
         kth[1] = b;
         float mag = fabsf(a) > fabsf(b) ? fabsf(a) : fabsf(b);
@@ -182,17 +204,20 @@ static void set_threads(int nthreads)
 /*
  * Index branch for a list of packed query rows.
  *   q_idx [total_q, h, d_idx] bf16, k_idx [total_k, d_idx] bf16
+ *   sink, local: forced blocks (see topk_blocks; 0, 0 = plain TopK)
  *   ids   [n_rows, h, top_k] int32 out, kth [n_rows, h, 2] float out
- *   (S_(k), S_(k+1), NaN when E <= k), near_tie [n_rows, h] uint8 out.
+ *   (last kept and first dropped ranked score, NaN when nothing is
+ *   dropped), near_tie [n_rows, h] uint8 out.
  * Returns 0, or -1 on a bad row / allocation failure.
  */
-int msa_oracle_index_topk(int num_seqs, const int32_t *cu_q, const int32_t *cu_k,
-                          int h, int d_idx, int B, int top_k,
-                          const uint16_t *q_idx, const uint16_t *k_idx,
-                          int64_t n_rows, const int64_t *rows,
-                          int32_t *ids, float *kth, uint8_t *near_tie, int nthreads)
+int msa_oracle_index_topk_forced(int num_seqs, const int32_t *cu_q, const int32_t *cu_k,
+                                 int h, int d_idx, int B, int top_k, int sink, int local,
+                                 const uint16_t *q_idx, const uint16_t *k_idx,
+                                 int64_t n_rows, const int64_t *rows,
+                                 int32_t *ids, float *kth, uint8_t *near_tie, int nthreads)
 {
     if (num_seqs < 1 || h < 1 || d_idx < 1 || B < 1 || top_k < 1) return -1;
+    if (sink < 0 || local < 0 || sink + local > top_k) return -1;
     set_threads(nthreads);
     int err = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -206,10 +231,21 @@ int msa_oracle_index_topk(int num_seqs, const int32_t *cu_q, const int32_t *cu_k
         if (!S) { err = 1; continue; }
         const uint16_t *qi = q_idx + (rows[i] * h + g) * (int64_t)d_idx;
         block_max_pool(&qp, qi, k_idx, d_idx, B, S);
-        if (topk_blocks(S, E, top_k, ids + task * top_k, kth + task * 2, near_tie + task)) err = 1;
+        if (topk_blocks(S, E, top_k, sink, local, ids + task * top_k, kth + task * 2, near_tie + task)) err = 1;
         free(S);
     }
     return err ? -1 : 0;
+}
+
+/* Plain TopK (no forced blocks). */
+int msa_oracle_index_topk(int num_seqs, const int32_t *cu_q, const int32_t *cu_k,
+                          int h, int d_idx, int B, int top_k,
+                          const uint16_t *q_idx, const uint16_t *k_idx,
+                          int64_t n_rows, const int64_t *rows,
+                          int32_t *ids, float *kth, uint8_t *near_tie, int nthreads)
+{
+    return msa_oracle_index_topk_forced(num_seqs, cu_q, cu_k, h, d_idx, B, top_k, 0, 0, q_idx, k_idx, n_rows, rows,
+                                        ids, kth, near_tie, nthreads);
 }
 
 /*

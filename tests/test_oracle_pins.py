@@ -335,3 +335,92 @@ def test_oracle_rejects_ineligible_or_duplicate_ids(oracle_lib):
     dup[50, 0, 1] = 0
     with pytest.raises(ValueError):
         oracle_lib.sparse_attention(inp, dup)
+
+
+# ---------------------------------------------------------------------------
+# Forced blocks (attention-sink and local-window option; 0, 0 = plain TopK).
+
+
+def bruteforce_forced(inp, sink, local):
+    """Exact block maxima (float64 of integer-valued products); forced blocks,
+    then a lexsort of the rest."""
+    wl = inp.wl
+    h, B, K = wl.num_kv_heads, wl.block_size, wl.top_k
+    qi, ki = f64(inp.q_idx), f64(inp.k_idx)
+    ids = np.full((wl.total_q, h, K), -1, np.int32)
+    for s in range(len(wl.seqlens_q)):
+        q0, q1 = inp.cu_seqlens_q[s], inp.cu_seqlens_q[s + 1]
+        k0, k1 = inp.cu_seqlens_k[s], inp.cu_seqlens_k[s + 1]
+        lq, lk = q1 - q0, k1 - k0
+        for r in range(lq):
+            p = lk - lq + r
+            E = p // B + 1
+            forced = sorted(set(range(min(sink, E))) | set(range(max(0, E - local), E)))
+            rest = np.array([j for j in range(E) if j not in forced], np.int64)
+            for g in range(h):
+                sc = ki[k0:k0 + p + 1] @ qi[q0 + r, g]
+                S = np.array([sc[j * B:min((j + 1) * B, p + 1)].max() for j in range(E)])
+                order = rest[np.lexsort((rest, -S[rest]))] if len(rest) else rest
+                m = min(K, E)
+                keep = sorted(forced + order[:m - len(forced)].tolist())
+                ids[q0 + r, g, :m] = keep
+    return ids
+
+
+@pytest.mark.parametrize("sink,local", [(1, 0), (0, 1), (1, 2), (2, 3)])
+def test_forced_blocks_equal_bruteforce(oracle_lib, sink, local):
+    sq, sk, h, di, B, K = (97, 1, 160), (97, 33, 160), 3, 4, 16, 5
+    rng = np.random.default_rng(11)
+    q_idx = rng.integers(-3, 4, size=(sum(sq), h, di)).astype(np.float32)
+    k_idx = rng.integers(-3, 4, size=(sum(sk), di)).astype(np.float32)
+    inp = make(sq, sk, h * 2, h, 16, di, B, K, q_idx=q_idx, k_idx=k_idx)
+    ids, _, _ = oracle_lib.index_topk(inp, sink=sink, local=local)
+    np.testing.assert_array_equal(ids, bruteforce_forced(inp, sink, local))
+
+
+def test_forced_blocks_closed_forms(oracle_lib):
+    n, h, B, K = 640, 2, 32, 4
+    rng = np.random.default_rng(2)
+    inp = make((n,), (n,), 4, h, 16, 8, B, K, seed=4)
+    plain, _, _ = oracle_lib.index_topk(inp)
+    # nothing forced: plain TopK
+    np.testing.assert_array_equal(oracle_lib.index_topk(inp, sink=0, local=0)[0], plain)
+    # sink + local = k: once E exceeds k the selection is the forced set, whatever the scores
+    ids, kth, tie = oracle_lib.index_topk(inp, sink=1, local=3)
+    for p in range(n):
+        E = p // B + 1
+        if E > K:
+            assert list(ids[p, 0]) == [0, E - 3, E - 2, E - 1], p
+            assert np.isnan(kth[p, 0]).all() and not tie[p].any()
+    # planted scores on non-forced blocks: forced blocks plus the best planted ones
+    values = {(g, j): float(rng.choice(np.arange(1, 200))) for g in range(h) for j in range(2, n // B - 2)}
+    q_idx, k_idx, offs = _planted(n, h, B, K, values)
+    inp = make((n,), (n,), h * 3, h, 16, 8, B, K, q_idx=q_idx, k_idx=k_idx)
+    ids, _, _ = oracle_lib.index_topk(inp, sink=1, local=1)
+    p = n - 1
+    E = p // B + 1
+    for g in range(h):
+        ranked = sorted(((val, j) for (gg, j), val in values.items() if gg == g and 0 < j < E - 1),
+                        key=lambda x: (-x[0], x[1]))
+        assert list(ids[p, g]) == sorted([0, E - 1] + [j for _, j in ranked[:K - 2]])
+
+
+def test_forced_blocks_invariants(oracle_lib):
+    inp = make((300, 45), (300, 45), 8, 2, 32, 16, 16, 6, seed=9)
+    sink, local = 2, 2
+    ids, _, _ = oracle_lib.index_topk(inp, sink=sink, local=local)
+    for row in range(inp.wl.total_q):
+        s = 0 if row < 300 else 1
+        p = row - inp.cu_seqlens_q[s]
+        E = p // 16 + 1
+        forced = set(range(min(sink, E))) | set(range(max(0, E - local), E))
+        for g in range(2):
+            sel = set(ids[row, g][ids[row, g] >= 0].tolist())
+            assert forced <= sel and len(sel) == min(6, E)
+            S = oracle_lib.block_scores(inp, row, g)
+            kept = [S[j] for j in sel - forced]
+            dropped = [S[j] for j in set(range(E)) - sel]
+            if kept and dropped:
+                assert min(kept) >= max(dropped)
+    with pytest.raises(ValueError):
+        oracle_lib.index_topk(inp, sink=4, local=3)   # more forced blocks than k
