@@ -113,20 +113,7 @@ size_t msa_workspace_size(int op, const msa_problem_t *problem) {
 
 msa_status_t msa_index_topk(const msa_problem_t *problem, const msa_bf16_t *q_idx, const msa_bf16_t *k_idx,
                             int32_t *topk_ids, void *workspace, size_t workspace_bytes, msa_stream_t stream) {
-    msa_status_t st = check_problem(problem);
-    if (st != MSA_SUCCESS) return st;
-    const msa_problem_t &p = *problem;
-    if (p.total_q == 0) return MSA_SUCCESS;
-    if (q_idx == nullptr || k_idx == nullptr || topk_ids == nullptr) return MSA_ERROR_INVALID_VALUE;
-    if ((st = index_support(p)) != MSA_SUCCESS) return st;
-    if ((st = check_ws(workspace, workspace_bytes, index_ws(p))) != MSA_SUCCESS) return st;
-    Shape s = to_shape(p);
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    float *scores = reinterpret_cast<float *>(workspace);
-    hipError_t e = (p.max_seqlen_q == 1) ? msa::launch_index_decode(s, q_idx, k_idx, scores, hs)
-                                         : msa::launch_index_prefill(s, q_idx, k_idx, scores, hs);
-    if (e != hipSuccess) return MSA_ERROR_LAUNCH;
-    return launched(msa::launch_topk_select(s, scores, topk_ids, hs));
+    return msa_index_topk_ex(problem, nullptr, nullptr, q_idx, k_idx, topk_ids, workspace, workspace_bytes, stream);
 }
 
 msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
@@ -188,19 +175,36 @@ void set_paged(Shape &s, const msa_paged_kv_t &pk) {
 msa_status_t msa_index_topk_paged(const msa_problem_t *problem, const msa_paged_kv_t *paged, const msa_bf16_t *q_idx,
                                   const msa_bf16_t *k_idx_pool, int32_t *topk_ids, void *workspace,
                                   size_t workspace_bytes, msa_stream_t stream) {
+    if (paged == nullptr) return MSA_ERROR_INVALID_VALUE;
+    return msa_index_topk_ex(problem, nullptr, paged, q_idx, k_idx_pool, topk_ids, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_index_topk_ex(const msa_problem_t *problem, const msa_select_options_t *options,
+                               const msa_paged_kv_t *paged, const msa_bf16_t *q_idx, const msa_bf16_t *k_idx,
+                               int32_t *topk_ids, void *workspace, size_t workspace_bytes, msa_stream_t stream) {
     msa_status_t st = check_problem(problem);
     if (st != MSA_SUCCESS) return st;
     const msa_problem_t &p = *problem;
+    if (options != nullptr &&
+        (options->sink_blocks < 0 || options->local_blocks < 0 ||
+         (long)options->sink_blocks + options->local_blocks > p.top_k))
+        return MSA_ERROR_INVALID_VALUE;
     if (p.total_q == 0) return MSA_SUCCESS;
-    if ((st = check_paged(p, paged)) != MSA_SUCCESS) return st;
-    if (q_idx == nullptr || k_idx_pool == nullptr || topk_ids == nullptr) return MSA_ERROR_INVALID_VALUE;
+    if (paged != nullptr && (st = check_paged(p, paged)) != MSA_SUCCESS) return st;
+    if (q_idx == nullptr || k_idx == nullptr || topk_ids == nullptr) return MSA_ERROR_INVALID_VALUE;
     if ((st = index_support(p)) != MSA_SUCCESS) return st;
     if ((st = check_ws(workspace, workspace_bytes, index_ws(p))) != MSA_SUCCESS) return st;
     Shape s = to_shape(p);
-    set_paged(s, *paged);
+    if (paged != nullptr) set_paged(s, *paged);
+    if (options != nullptr) {
+        s.sink = options->sink_blocks;
+        s.local = options->local_blocks;
+    }
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     float *scores = reinterpret_cast<float *>(workspace);
-    if (msa::launch_index_decode(s, q_idx, k_idx_pool, scores, hs) != hipSuccess) return MSA_ERROR_LAUNCH;
+    hipError_t e = (p.max_seqlen_q == 1) ? msa::launch_index_decode(s, q_idx, k_idx, scores, hs)
+                                         : msa::launch_index_prefill(s, q_idx, k_idx, scores, hs);
+    if (e != hipSuccess) return MSA_ERROR_LAUNCH;
     return launched(msa::launch_topk_select(s, scores, topk_ids, hs));
 }
 

@@ -15,6 +15,9 @@ struct Shape {
     // table[s * table_stride + j]; null table = contiguous packed cache.
     const int32_t *table = nullptr;
     int table_stride = 0, num_pages = 0;
+    // Forced blocks in every selection: the first `sink` and the last `local`
+    // eligible blocks (0, 0 = plain TopK).
+    int sink = 0, local = 0;
 };
 
 // Block-level scores workspace: [total_q, h, e_stride] float32.

@@ -6,7 +6,10 @@
 // Exact selection.  Scores are mapped to order-preserving uint32 keys (-0.0
 // folded onto +0.0) and the k-th largest key T is located; all keys > T are
 // kept, then the lowest-indexed keys == T until k are kept (ties go to the
-// lower block id).  Ids are written in ascending order, which falls out of
+// lower block id).  Optionally the first `sink` and the last `local` eligible
+// blocks are forced in (an option, not the pages' method: "MiniMax Goes
+// Sparse", section 2, speculates that an attention sink may take the place of
+// the dropped sliding-window branch); they get a key above every score.  Ids are written in ascending order, which falls out of
 // giving every thread a contiguous run of block indices and prefix-summing
 // per-thread counts.
 //
@@ -44,17 +47,23 @@ __device__ __forceinline__ RowInfo row_info(long pair, const int32_t *cu_q, cons
     return RowInfo{p / B + 1, pair};
 }
 
+// Keys of blocks t*VPT .. t*VPT+VPT-1 (0 past E).  Forced blocks (the first
+// `sink` and the last `local` eligible ones) get the largest key, above that
+// of any score, so they are always kept; the caller guarantees
+// sink + local <= k.
 template <int VPT>
-__device__ __forceinline__ void load_keys(uint32_t (&key)[VPT], const float *src, int t, int E) {
+__device__ __forceinline__ void load_keys(uint32_t (&key)[VPT], const float *src, int t, int E, int sink, int local) {
 #pragma unroll
     for (int v = 0; v < VPT; v += 4) {
         const int i = t * VPT + v;
         float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
         if (i < E) f = *reinterpret_cast<const float4 *>(src + i);
-        key[v + 0] = (i + 0 < E) ? order_key(f.x) : 0u;
-        key[v + 1] = (i + 1 < E) ? order_key(f.y) : 0u;
-        key[v + 2] = (i + 2 < E) ? order_key(f.z) : 0u;
-        key[v + 3] = (i + 3 < E) ? order_key(f.w) : 0u;
+        const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = i + u;
+            key[v + u] = (j < E) ? ((j < sink || j >= E - local) ? 0xffffffffu : order_key(fv[u])) : 0u;
+        }
     }
 }
 
@@ -81,7 +90,8 @@ template <int VPT>
 __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict__ scores, int e_stride,
                                                         const int32_t *__restrict__ cu_q,
                                                         const int32_t *__restrict__ cu_k, int num_seqs, int total_q,
-                                                        int h, int B, int k, int32_t *__restrict__ ids) {
+                                                        int h, int B, int k, int sink, int local,
+                                                        int32_t *__restrict__ ids) {
     const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (pair >= (long)total_q * h) return;   // uniform per wave
     const int t = threadIdx.x & 63;
@@ -93,7 +103,7 @@ __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict_
         return;
     }
     uint32_t key[VPT];
-    load_keys<VPT>(key, scores + pair * e_stride, t, E);
+    load_keys<VPT>(key, scores + pair * e_stride, t, E, sink, local);
 
     // common prefix of the largest and smallest valid key
     uint32_t mx = 0u, mn = 0xffffffffu;
@@ -183,7 +193,8 @@ template <int VPT>
 __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict__ scores, int e_stride,
                                                          const int32_t *__restrict__ cu_q,
                                                          const int32_t *__restrict__ cu_k, int num_seqs, int total_q,
-                                                         int h, int B, int k, int32_t *__restrict__ ids) {
+                                                         int h, int B, int k, int sink, int local,
+                                                         int32_t *__restrict__ ids) {
     __shared__ int hist[kBins];
     __shared__ int red[kNW];
     __shared__ uint32_t bc[4];
@@ -199,7 +210,7 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
         return;
     }
     uint32_t key[VPT];
-    load_keys<VPT>(key, scores + pair * e_stride, t, E);
+    load_keys<VPT>(key, scores + pair * e_stride, t, E, sink, local);
 
     uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
@@ -304,7 +315,8 @@ template <int VPT>
 hipError_t launch_wave(const Shape &s, const float *scores, int32_t *ids, hipStream_t st) {
     const long pairs = (long)s.total_q * s.h;
     hipLaunchKernelGGL((topk_select_wave<VPT>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, scores,
-                       score_stride(s), s.cu_q, s.cu_k, s.num_seqs, s.total_q, s.h, s.B, s.top_k, ids);
+                       score_stride(s), s.cu_q, s.cu_k, s.num_seqs, s.total_q, s.h, s.B, s.top_k, s.sink, s.local,
+                       ids);
     return hipGetLastError();
 }
 
@@ -312,7 +324,7 @@ template <int VPT>
 hipError_t launch_block(const Shape &s, const float *scores, int32_t *ids, hipStream_t st) {
     const long pairs = (long)s.total_q * s.h;
     hipLaunchKernelGGL((topk_select_block<VPT>), dim3((unsigned)pairs), dim3(kNT), 0, st, scores, score_stride(s),
-                       s.cu_q, s.cu_k, s.num_seqs, s.total_q, s.h, s.B, s.top_k, ids);
+                       s.cu_q, s.cu_k, s.num_seqs, s.total_q, s.h, s.B, s.top_k, s.sink, s.local, ids);
     return hipGetLastError();
 }
 

@@ -170,3 +170,14 @@ def sparse_attention_paged(dp: DeviceProblem, pc: PagedCache, ids, out=None, lse
     msa.msa_sparse_attn_decode_paged(dp.problem, pc.paged, dp.q, pc.k_pool, pc.v_pool, ids, dp.wl.scale, out, lse,
                                      dp.ws_attn, stream)
     return out, lse
+
+
+def index_topk_forced(dp: DeviceProblem, sink_blocks: int, local_blocks: int, ids=None, pc: PagedCache | None = None,
+                      stream=None) -> torch.Tensor:
+    """Index branch with forced sink / local blocks (contiguous cache, or the paged one in `pc`)."""
+    if ids is None:
+        ids = alloc_ids(dp)
+    k_idx = dp.k_idx if pc is None else pc.k_idx_pool
+    msa.msa_index_topk_ex(dp.problem, dp.q_idx, k_idx, ids, dp.ws_index, sink_blocks, local_blocks,
+                          None if pc is None else pc.paged, stream)
+    return ids

@@ -60,6 +60,13 @@ class msa_paged_kv_t(ctypes.Structure):
     ]
 
 
+class msa_select_options_t(ctypes.Structure):
+    _fields_ = [
+        ("sink_blocks", ctypes.c_int32),
+        ("local_blocks", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -85,6 +92,8 @@ def load():
     lib.msa_sparse_attn_decode_paged.argtypes = [prob, paged, P, P, P, P, ctypes.c_float, P, P, P, S, P]
     lib.msa_sparse_attn_decode_paged.restype = ctypes.c_int
     i32 = ctypes.c_int32
+    lib.msa_index_topk_ex.argtypes = [prob, ctypes.POINTER(msa_select_options_t), paged, P, P, P, P, S, P]
+    lib.msa_index_topk_ex.restype = ctypes.c_int
     lib.msa_kv_append_paged.argtypes = [i32, i32, i32, i32, ctypes.c_int64, P, P, P, P, P, P, P, P]
     lib.msa_kv_append_paged.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [ctypes.c_int, prob]
@@ -204,3 +213,13 @@ def msa_kv_append_paged(slot_mapping, k, v, k_idx, k_pool, v_pool, k_idx_pool, s
     _check(load().msa_kv_append_paged(n, h, d, int(k_idx.shape[1]), int(k_pool.shape[0]), _ptr(slot_mapping),
                                       _ptr(k), _ptr(v), _ptr(k_idx), _ptr(k_pool), _ptr(v_pool), _ptr(k_idx_pool),
                                       _stream(stream)), "msa_kv_append_paged")
+
+
+def msa_index_topk_ex(problem, q_idx, k_idx, topk_ids, workspace=None, sink_blocks=0, local_blocks=0, paged=None,
+                      stream=None):
+    """msa_index_topk with forced sink / local blocks, over a contiguous or (paged=...) a paged cache."""
+    opt = msa_select_options_t(int(sink_blocks), int(local_blocks))
+    _check(load().msa_index_topk_ex(ctypes.byref(problem), ctypes.byref(opt),
+                                    ctypes.byref(paged) if paged is not None else None, _ptr(q_idx), _ptr(k_idx),
+                                    _ptr(topk_ids), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "msa_index_topk_ex")

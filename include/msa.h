@@ -206,6 +206,34 @@ msa_status_t msa_kv_append_paged(int32_t num_tokens, int32_t num_kv_heads, int32
                                  const msa_bf16_t *v, const msa_bf16_t *k_idx, msa_bf16_t *k_pool,
                                  msa_bf16_t *v_pool, msa_bf16_t *k_idx_pool, msa_stream_t stream);
 
+/*
+ * Selection options.  The pages' method is pure TopK (all fields 0).  Their
+ * authors speculate that the dropped sliding-window branch may be replaced by
+ * an attention sink or a local window ("MiniMax Goes Sparse", section 2, on
+ * the three trade-offs; "MiniMax M3 MSA vs Step 3.7 Flash MFA", section on
+ * waiting for the technical report).  These options force such blocks into
+ * every selection:
+ *   sink_blocks   blocks 0 .. sink_blocks-1 (those that are eligible);
+ *   local_blocks  the local_blocks eligible blocks ending at the query's own
+ *                 (diagonal) block E-1.
+ * The other min(k, E) - |forced| slots go to the remaining blocks in the
+ * usual (score descending, block id ascending) order; ids stay ascending.
+ * Requires sink_blocks, local_blocks >= 0 and sink_blocks + local_blocks <=
+ * top_k.  A dense-fallback layer needs no option: top_k >= ceil(max_len / B)
+ * selects every eligible block, i.e. dense causal attention.
+ */
+typedef struct {
+    int32_t sink_blocks;
+    int32_t local_blocks;
+} msa_select_options_t;
+
+/* msa_index_topk with selection options (NULL = plain TopK) over a
+ * contiguous cache (paged == NULL) or a paged one (decode only, see
+ * msa_paged_kv_t).  Same workspace as msa_index_topk. */
+msa_status_t msa_index_topk_ex(const msa_problem_t *problem, const msa_select_options_t *options,
+                               const msa_paged_kv_t *paged, const msa_bf16_t *q_idx, const msa_bf16_t *k_idx,
+                               int32_t *topk_ids, void *workspace, size_t workspace_bytes, msa_stream_t stream);
+
 /* Workspace bytes an entry point needs for `problem` (0 if none).  Returns
  * (size_t)-1 when the problem is invalid or unsupported for that op. */
 size_t msa_workspace_size(int op, const msa_problem_t *problem);

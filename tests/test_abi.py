@@ -177,3 +177,18 @@ def test_append_rejects(lib):
     assert call(slots=None) == msa.MSA_ERROR_INVALID_VALUE
     assert call(k=FAKE + 8) == msa.MSA_ERROR_INVALID_VALUE   # rows must be 16-byte aligned
     assert call(n=0, slots=None, k=None) == msa.MSA_SUCCESS   # nothing to do
+
+
+def test_select_options_rejects(lib):
+    p = prob()
+    need = lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p))
+
+    def call(sink, local, p=p, paged=None):
+        opt = msa.msa_select_options_t(sink, local)
+        return lib.msa_index_topk_ex(ctypes.byref(p), ctypes.byref(opt), paged, FAKE, FAKE, FAKE, None, need, None)
+
+    assert call(-1, 0) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(0, -1) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(3, 2) == msa.MSA_ERROR_INVALID_VALUE          # 5 forced blocks > top_k = 4
+    assert call(2, 2) == msa.MSA_ERROR_WORKSPACE               # valid options; fails later on the workspace
+    assert call(1, 1, paged=ctypes.byref(paged())) == msa.MSA_ERROR_NOT_SUPPORTED   # paged needs decode shapes
