@@ -51,6 +51,9 @@ def _load():
         lib.msa_oracle_sparse_attention.argtypes = [i32, P, P, i32, i32, i32, i32, i32, P, P, P, P,
                                                     ctypes.c_float, i64, P, P, P, i32]
         lib.msa_oracle_sparse_attention.restype = i32
+        lib.msa_oracle_sparse_attention_backward.argtypes = [i32, P, P, i32, i32, i32, i32, i32, P, P, P, P,
+                                                             ctypes.c_float, P, P, P, P, i32]
+        lib.msa_oracle_sparse_attention_backward.restype = i32
         _lib = lib
     return _lib
 
@@ -132,3 +135,28 @@ def sparse_attention(inp, ids, rows=None, scale=None, threads: int = 0):
     if rc != 0:
         raise ValueError("oracle sparse_attention rejected its input")
     return out, lse
+
+
+def sparse_attention_backward(inp, ids, dout, scale=None, threads: int = 0):
+    """Oracle backward of the sparse branch with the selection ``ids``
+    [total_q, h, k] held fixed; ``dout`` [total_q, H, d] holds bf16 bits.
+    Returns (dq [total_q, H, d], dk [total_k, h, d], dv [total_k, h, d]) float32."""
+    wl = inp.wl
+    ids = _c(ids, np.int32)
+    tq, tk = int(inp.cu_seqlens_q[-1]), int(inp.cu_seqlens_k[-1])
+    H, h, d = wl.num_heads, wl.num_kv_heads, wl.head_dim
+    if ids.shape[:2] != (tq, h):
+        raise ValueError("ids must be [total_q, h, top_k]")
+    dq = np.empty((tq, H, d), np.float32)
+    dk = np.empty((tk, h, d), np.float32)
+    dv = np.empty((tk, h, d), np.float32)
+    cu_q, cu_k = _c(inp.cu_seqlens_q, np.int32), _c(inp.cu_seqlens_k, np.int32)
+    q, kk, v, do = (_c(x, np.uint16) for x in (inp.q, inp.k, inp.v, dout))
+    sc = wl.scale if scale is None else scale
+    rc = _load().msa_oracle_sparse_attention_backward(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), H, h, d,
+                                                      wl.block_size, ids.shape[2], _ptr(q), _ptr(kk), _ptr(v),
+                                                      _ptr(ids), ctypes.c_float(sc), _ptr(do), _ptr(dq), _ptr(dk),
+                                                      _ptr(dv), threads)
+    if rc != 0:
+        raise ValueError("oracle sparse_attention_backward rejected its input")
+    return dq, dk, dv

@@ -331,3 +331,105 @@ int msa_oracle_sparse_attention(int num_seqs, const int32_t *cu_q, const int32_t
     }
     return err ? -1 : 0;
 }
+
+/*
+ * Backward of the sparse branch for a fixed selection (the ids are an input
+ * and are not differentiated).  With P_t the softmax weights of one (row,
+ * head) over its visible selected tokens T, O = sum_t P_t v_t and dO the
+ * incoming gradient of O, the chain rule through softmax gives
+ *     dP_t = dO . v_t,   D = sum_t P_t dP_t,   dS_t = P_t (dP_t - D),
+ *     dq   = scale * sum_t dS_t k_t,
+ *     dk_t += scale * dS_t q,   dv_t += P_t dO   (summed over every row and
+ *     head of the group that sees token t).
+ * The pages define only the forward pass; training through the sparse branch
+ * is an open point there ([P4] section "waiting for the technical report":
+ * hard or soft top-k in training is unknown).  This is the plain gradient of
+ * the forward above with the selection held fixed.
+ *   q [total_q, H, d], k/v [total_k, h, d], dout [total_q, H, d] bf16
+ *   ids [total_q, h, top_k] (every row)
+ *   dq [total_q, H, d], dk/dv [total_k, h, d] float32 out (fully written).
+ * Parallel over groups (each thread owns its group's dk/dv).  Returns 0 or -1.
+ */
+int msa_oracle_sparse_attention_backward(int num_seqs, const int32_t *cu_q, const int32_t *cu_k,
+                                         int H, int h, int d, int B, int top_k,
+                                         const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                         const int32_t *ids, float scale, const uint16_t *dout,
+                                         float *dq, float *dk, float *dv, int nthreads)
+{
+    if (num_seqs < 1 || h < 1 || H < h || H % h || d < 1 || B < 1 || top_k < 1) return -1;
+    const int G = H / h;
+    const int64_t total_q = cu_q[num_seqs], total_k = cu_k[num_seqs];
+    memset(dq, 0, (size_t)total_q * H * d * sizeof(float));
+    memset(dk, 0, (size_t)total_k * h * d * sizeof(float));
+    memset(dv, 0, (size_t)total_k * h * d * sizeof(float));
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int g = 0; g < h; ++g) {
+        float *P = (float *)malloc((size_t)top_k * B * sizeof(float));
+        float *dP = (float *)malloc((size_t)top_k * B * sizeof(float));
+        int64_t *tok = (int64_t *)malloc((size_t)top_k * B * sizeof(int64_t));
+        if (!P || !dP || !tok) { err = 1; free(P); free(dP); free(tok); continue; }
+        for (int64_t row = 0; row < total_q; ++row) {
+            query_pos_t qp;
+            if (locate(num_seqs, cu_q, cu_k, row, &qp)) { err = 1; break; }
+            const int64_t E = qp.p / B + 1;
+            const int32_t *sel = ids + (row * h + g) * (int64_t)top_k;
+            int bad = 0;
+            for (int a = 0; a < top_k; ++a) {
+                if (sel[a] < -1 || sel[a] >= E) bad = 1;
+                for (int b = 0; b < a; ++b)
+                    if (sel[a] >= 0 && sel[a] == sel[b]) bad = 1;
+            }
+            if (bad) { err = 1; break; }
+            int64_t n = 0;
+            for (int a = 0; a < top_k; ++a) {
+                if (sel[a] < 0) continue;
+                for (int64_t t = (int64_t)sel[a] * B; t < (int64_t)(sel[a] + 1) * B && t <= qp.p; ++t)
+                    tok[n++] = qp.k0 + t;
+            }
+            for (int head = g * G; head < (g + 1) * G; ++head) {
+                const uint16_t *qr = q + (row * H + head) * (int64_t)d;
+                const uint16_t *dor = dout + (row * H + head) * (int64_t)d;
+                /* forward weights */
+                float M = -INFINITY;
+                for (int64_t a = 0; a < n; ++a) {
+                    const uint16_t *kt = k + (tok[a] * h + g) * (int64_t)d;
+                    float s = 0.0f;
+                    for (int c = 0; c < d; ++c) s += bf16_to_float(qr[c]) * bf16_to_float(kt[c]);
+                    P[a] = s * scale;
+                    if (P[a] > M) M = P[a];
+                }
+                float Z = 0.0f;
+                for (int64_t a = 0; a < n; ++a) {
+                    P[a] = expf(P[a] - M);
+                    Z += P[a];
+                }
+                for (int64_t a = 0; a < n; ++a) P[a] /= Z;
+                /* dP_t = dO . v_t and D = sum_t P_t dP_t */
+                float Dsum = 0.0f;
+                for (int64_t a = 0; a < n; ++a) {
+                    const uint16_t *vt = v + (tok[a] * h + g) * (int64_t)d;
+                    float s = 0.0f;
+                    for (int c = 0; c < d; ++c) s += bf16_to_float(dor[c]) * bf16_to_float(vt[c]);
+                    dP[a] = s;
+                    Dsum += P[a] * s;
+                }
+                float *dqr = dq + (row * H + head) * (int64_t)d;
+                for (int64_t a = 0; a < n; ++a) {
+                    const float dS = P[a] * (dP[a] - Dsum);
+                    const uint16_t *kt = k + (tok[a] * h + g) * (int64_t)d;
+                    float *dkt = dk + (tok[a] * h + g) * (int64_t)d;
+                    float *dvt = dv + (tok[a] * h + g) * (int64_t)d;
+                    for (int c = 0; c < d; ++c) {
+                        dqr[c] += scale * dS * bf16_to_float(kt[c]);
+                        dkt[c] += scale * dS * bf16_to_float(qr[c]);
+                        dvt[c] += P[a] * bf16_to_float(dor[c]);
+                    }
+                }
+            }
+        }
+        free(P); free(dP); free(tok);
+    }
+    return err ? -1 : 0;
+}
