@@ -107,6 +107,9 @@ size_t msa_workspace_size(int op, const msa_problem_t *problem) {
             if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
             if (p.max_seqlen_q != 1 || p.total_q != p.num_seqs) return (size_t)-1;
             return msa::decode_workspace_bytes(to_shape(p));
+        case MSA_OP_SPARSE_ATTN_BACKWARD:
+            if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
+            return msa::backward_workspace_bytes(to_shape(p));
     }
     return (size_t)-1;
 }
@@ -132,6 +135,26 @@ msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf1
     if ((st = check_ws(workspace, workspace_bytes, msa::prefill_workspace_bytes(s))) != MSA_SUCCESS) return st;
     return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+msa_status_t msa_sparse_attn_prefill_backward(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
+                                              const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
+                                              const msa_bf16_t *out, const float *lse, const msa_bf16_t *dout,
+                                              msa_bf16_t *dq, msa_bf16_t *dk, msa_bf16_t *dv, void *workspace,
+                                              size_t workspace_bytes, msa_stream_t stream) {
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if (q == nullptr || k == nullptr || v == nullptr || topk_ids == nullptr || out == nullptr || lse == nullptr ||
+        dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
+    if ((st = attn_support(p)) != MSA_SUCCESS) return st;
+    Shape s = to_shape(p);
+    if ((st = check_ws(workspace, workspace_bytes, msa::backward_workspace_bytes(s))) != MSA_SUCCESS) return st;
+    return launched(msa::launch_attn_backward(s, q, k, v, topk_ids, softmax_scale, out, lse, dout, dq, dk, dv,
+                                              workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k_cache,

@@ -44,6 +44,12 @@ hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t
 hipError_t launch_kv_append(int n, int h, int d, int d_idx, long long pool_rows, const int32_t *slots,
                             const uint16_t *k, const uint16_t *v, const uint16_t *k_idx, uint16_t *k_pool,
                             uint16_t *v_pool, uint16_t *k_idx_pool, hipStream_t st);
+// Backward of the sparse branch (prefill, selection fixed).
+size_t backward_workspace_bytes(const Shape &s);
+hipError_t launch_attn_backward(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const int32_t *ids, float scale, const uint16_t *out, const float *lse,
+                                const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv, void *ws,
+                                hipStream_t st);
 int decode_splits(const Shape &s);
 size_t decode_workspace_bytes(const Shape &s);
 hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,

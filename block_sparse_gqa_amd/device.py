@@ -181,3 +181,16 @@ def index_topk_forced(dp: DeviceProblem, sink_blocks: int, local_blocks: int, id
     msa.msa_index_topk_ex(dp.problem, dp.q_idx, k_idx, ids, dp.ws_index, sink_blocks, local_blocks,
                           None if pc is None else pc.paged, stream)
     return ids
+
+
+def sparse_attention_backward(dp: DeviceProblem, ids, out, lse, dout, ws=None, stream=None):
+    """Gradients (dq, dk, dv) of the prefill sparse branch for the fixed ids."""
+    wl = dp.wl
+    if ws is None:
+        ws = _workspace(msa.MSA_OP_SPARSE_ATTN_BACKWARD, dp.problem, dp.q.device)
+    dq = torch.empty_like(dp.q)
+    dk = torch.empty_like(dp.k)
+    dv = torch.empty_like(dp.v)
+    msa.msa_sparse_attn_prefill_backward(dp.problem, dp.q, dp.k, dp.v, ids, wl.scale, out, lse, dout, dq, dk, dv, ws,
+                                         stream)
+    return dq, dk, dv

@@ -24,6 +24,7 @@ MSA_ERROR_LAUNCH = 4
 MSA_OP_INDEX_TOPK = 0
 MSA_OP_SPARSE_ATTN_PREFILL = 1
 MSA_OP_SPARSE_ATTN_DECODE = 2
+MSA_OP_SPARSE_ATTN_BACKWARD = 3
 
 SIZE_MAX = (1 << 64) - 1
 
@@ -96,6 +97,8 @@ def load():
     lib.msa_index_topk_ex.restype = ctypes.c_int
     lib.msa_kv_append_paged.argtypes = [i32, i32, i32, i32, ctypes.c_int64, P, P, P, P, P, P, P, P]
     lib.msa_kv_append_paged.restype = ctypes.c_int
+    lib.msa_sparse_attn_prefill_backward.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, S, P]
+    lib.msa_sparse_attn_prefill_backward.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [ctypes.c_int, prob]
     lib.msa_workspace_size.restype = S
     lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -223,3 +226,11 @@ def msa_index_topk_ex(problem, q_idx, k_idx, topk_ids, workspace=None, sink_bloc
                                     ctypes.byref(paged) if paged is not None else None, _ptr(q_idx), _ptr(k_idx),
                                     _ptr(topk_ids), _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "msa_index_topk_ex")
+
+
+def msa_sparse_attn_prefill_backward(problem, q, k, v, topk_ids, softmax_scale, out, lse, dout, dq, dk, dv,
+                                     workspace=None, stream=None):
+    _check(load().msa_sparse_attn_prefill_backward(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_ids),
+                                                   float(softmax_scale), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                                   _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
+                                                   _stream(stream)), "msa_sparse_attn_prefill_backward")

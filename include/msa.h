@@ -62,7 +62,8 @@ typedef enum {
 typedef enum {
     MSA_OP_INDEX_TOPK = 0,
     MSA_OP_SPARSE_ATTN_PREFILL = 1,
-    MSA_OP_SPARSE_ATTN_DECODE = 2
+    MSA_OP_SPARSE_ATTN_DECODE = 2,
+    MSA_OP_SPARSE_ATTN_BACKWARD = 3
 } msa_op_t;
 
 typedef struct {
@@ -149,6 +150,37 @@ msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16
                                     const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out,
                                     float *lse, void *workspace, size_t workspace_bytes,
                                     msa_stream_t stream);
+
+/*
+ * Backward of the sparse branch, prefill, with the selection held fixed (the
+ * ids are constants, not differentiated).  The pages define the forward pass
+ * only and leave open whether training uses a hard or soft top-k ("MiniMax
+ * M3 MSA vs Step 3.7 Flash MFA", section on waiting for the technical
+ * report); this is the gradient of msa_sparse_attn_prefill's output for the
+ * given ids:
+ *     P_t = exp(scale q.k_t - lse),  dS_t = P_t (dO.v_t - dO.O),
+ *     dq = scale sum_t dS_t k_t,  dk_t = scale sum dS_t q,  dv_t = sum P_t dO
+ * (dk, dv summed over every row and head of the group that sees token t).
+ *
+ * q, out, dout [total_q, H, d] bf16; k, v [total_k, h, d] bf16;
+ * topk_ids [total_q, h, top_k] as for msa_sparse_attn_prefill;
+ * lse [total_q, H] float32 from the forward call (required);
+ * dq [total_q, H, d], dk, dv [total_k, h, d] bf16, written (tokens that no row
+ * sees get zero dk/dv).
+ * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_BACKWARD)
+ * bytes, 16-byte aligned: dO.O per row, one bf16 partial of dq per (row,
+ * selected slot, head) -- total_q * top_k * H * d * 2 bytes, the bulk of it
+ * (8.6 GB for 32K tokens, 32 heads, k = 32) -- and the per-(group, block)
+ * lists of selecting queries.  dk/dv sums run in list order, which atomics
+ * fix at run time, so they are not bitwise reproducible from call to call
+ * (within rounding); dq is.  Needs H/h <= 32 and total_q * top_k < 2^31.
+ */
+msa_status_t msa_sparse_attn_prefill_backward(const msa_problem_t *problem, const msa_bf16_t *q,
+                                              const msa_bf16_t *k, const msa_bf16_t *v, const int32_t *topk_ids,
+                                              float softmax_scale, const msa_bf16_t *out, const float *lse,
+                                              const msa_bf16_t *dout, msa_bf16_t *dq, msa_bf16_t *dk,
+                                              msa_bf16_t *dv, void *workspace, size_t workspace_bytes,
+                                              msa_stream_t stream);
 
 /*
  * Paged KV cache (decode).  The pages keep the cache in the native GQA

@@ -192,3 +192,20 @@ def test_select_options_rejects(lib):
     assert call(3, 2) == msa.MSA_ERROR_INVALID_VALUE          # 5 forced blocks > top_k = 4
     assert call(2, 2) == msa.MSA_ERROR_WORKSPACE               # valid options; fails later on the workspace
     assert call(1, 1, paged=ctypes.byref(paged())) == msa.MSA_ERROR_NOT_SUPPORTED   # paged needs decode shapes
+
+
+def test_backward_rejects(lib):
+    bwd = lib.msa_sparse_attn_prefill_backward
+    p = prob()
+    need = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_BACKWARD, ctypes.byref(p))
+    assert 0 < need < msa.SIZE_MAX
+
+    def call(p=p, lse=FAKE, dout=FAKE, scale=0.088, ws=FAKE, ws_bytes=need):
+        return bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE, lse, dout, FAKE, FAKE, FAKE,
+                   ws, ws_bytes, None)
+
+    assert call(lse=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(dout=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(scale=0.0) == msa.MSA_ERROR_INVALID_VALUE
+    assert call(ws_bytes=need - 1) == msa.MSA_ERROR_WORKSPACE
+    assert call(p=prob(head_dim=96)) == msa.MSA_ERROR_NOT_SUPPORTED
