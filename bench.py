@@ -179,6 +179,34 @@ def paged_decode(inp, dp, ids_contig, contig, steps, warmup):
             "page_in_ms": t_append, "page_in_GB_per_s": append_bytes / (t_append * 1e-3) / 1e9}
 
 
+def prefill_backward(dp, bufs, fwd, steps):
+    """Backward of the sparse branch (selection fixed) for the prefill step,
+    on the forward's own ids, out and lse.  Reported beside the headline."""
+    import torch
+
+    from block_sparse_gqa_amd import device, msa
+    ids, out, lse = bufs
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    dout = torch.randn(out.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    ws = device._workspace(msa.MSA_OP_SPARSE_ATTN_BACKWARD, dp.problem, dp.q.device)
+    device.sparse_attention_backward(dp, ids, out, lse, dout, ws)   # warm-up
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(steps):
+        device.sparse_attention_backward(dp, ids, out, lse, dout, ws)
+    e[1].record()
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / steps
+    # S (recomputed), dP, dV, dK, dQ: five products of 2 d flop per (head, visible token)
+    flops = 2.5 * (fwd["sparse_attn_TFLOP_per_s"] * fwd["sparse_attn_ms"] * 1e-3)   # forward: S and P.V
+    res = {"ms": ms, "algorithmic_TFLOP": flops, "TFLOP_per_s": flops / (ms * 1e-3),
+           "frac_mfma_peak": flops / (ms * 1e-3) / MFMA_BF16_PEAK_TFLOPS, "workspace_GB": ws.numel() / 1e9}
+    del ws, dout
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +214,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workloads", default=",".join(WORKLOADS))
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the sparse-branch backward measurement (reported beside the headline, not in it)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement (reported beside the headline, not in it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -292,6 +322,12 @@ def main():
     roofline = {"bound": kbound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": measured_traffic(*ksrc) if ksrc else None,
                 "traffic_unit": "bytes per launch", "avg_launch_ms": kms}
+
+    if not args.no_backward:
+        for name in names:
+            if not inputs[name].wl.is_decode:
+                results[name]["backward"] = prefill_backward(dps[name], bufs[name], results[name],
+                                                             max(args.steps // 2, 3))
 
     if not args.no_paged:
         for name in names:
