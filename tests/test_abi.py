@@ -209,3 +209,11 @@ def test_backward_rejects(lib):
     assert call(scale=0.0) == msa.MSA_ERROR_INVALID_VALUE
     assert call(ws_bytes=need - 1) == msa.MSA_ERROR_WORKSPACE
     assert call(p=prob(head_dim=96)) == msa.MSA_ERROR_NOT_SUPPORTED
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without the built library, loading raises."""
+    monkeypatch.setattr(msa, "_lib", None)
+    monkeypatch.setattr(msa, "LIB_PATH", str(tmp_path / "libmsa.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        msa.load()

@@ -95,3 +95,23 @@ def test_backward_untouched_tokens_zero():
             j = gids[r, g, 0]
             used[j * 64:min(j * 64 + 64, r + 1)] = True
         assert not dkh[~used, g].any() and not dvh[~used, g].any()
+
+
+@pytest.mark.timeout(300)
+def test_backward_repeat():
+    """dq is bitwise reproducible (per-slot partials summed in slot order); dk
+    and dv follow the run-time order of the selection lists and agree to
+    rounding."""
+    from block_sparse_gqa_amd import device
+    inp = synth.custom((777,), (777,), 16, 4, 128, 64, 64, 5, seed=5, name="bwd_repeat")
+    dp = device.upload(inp)
+    ids, out, lse = device.forward(dp)
+    dout = device.to_device_bf16(synth.f32_to_bf16_bits(
+        np.random.default_rng(2).standard_normal(inp.q.shape).astype(np.float32)))
+    a = device.sparse_attention_backward(dp, ids, out, lse, dout)
+    b = device.sparse_attention_backward(dp, ids, out, lse, dout)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    for x, y, n in ((a[1], b[1], "dk"), (a[2], b[2], "dv")):
+        xf, yf = x.float(), y.float()
+        assert float((xf - yf).abs().max()) <= 2 ** -7 * float(xf.abs().max()), n
