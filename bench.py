@@ -286,10 +286,12 @@ def main():
         ids = bufs[name][0]
         t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[name]]))
         t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in ev[name]]))
+        per_step = np.array([e[0].elapsed_time(e[2]) for e in ev[name]])
         alg = algorithmic(inp, dp, ids)
         wl = inp.wl
         total_tokens += wl.total_q
         r = {"tokens": wl.total_q, "ms": t_idx + t_att, "tokens_per_s": wl.total_q / ((t_idx + t_att) * 1e-3),
+             "ms_median": float(np.median(per_step)), "ms_min": float(per_step.min()),
              "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "selected_tokens": alg["selected_tokens"],
              "workload": wl.description}
         if wl.is_decode:
@@ -335,6 +337,20 @@ def main():
                 results[name]["paged"] = paged_decode(inputs[name], dps[name], bufs[name][0], results[name],
                                                       max(args.steps, 5), args.warmup)
 
+    # achievable HBM rate on this GPU: a plain 4 GiB device-to-device copy (read + write)
+    src = torch.empty(1 << 32, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    ce[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 32) * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -357,6 +373,7 @@ def main():
                    **{n: results[n]["workload"] for n in names}},
         "results": results,
         "roofline": roofline,
+        "ceilings": {"hbm_copy_GB_per_s": copy_gbs, "note": "device-to-device copy of 4 GiB, read + write bytes"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
