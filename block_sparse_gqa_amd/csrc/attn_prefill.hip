@@ -10,28 +10,30 @@
 // their selected blocks and streams each union block through LDS once, as
 // 64-token K and V sub-blocks.
 //
-// Staging.  A 4-stage LDS ring is filled with direct global->LDS loads
-// (global_load_lds_dwordx4: lane i of a load writes base + 16*i), so several
-// sub-blocks are in flight per workgroup without holding staging registers.
-// Row strides are padded (K: 2d+16 bytes, V: 2d+64 bytes) so that the K
-// operand reads and the transposing V reads are bank-conflict free; pad
-// slots are filled by the same loads and never read.  Ring reads are issued
-// in inline asm (each block waits for its own results) so the compiler does
-// not serialise them behind the in-flight ring loads.  Stages are handed
-// between waves with LDS flags and counters instead of workgroup barriers
-// (the protocol is described at the loop), so the waves sharing a SIMD drift
-// apart and overlap one another's MFMA and VALU work.
+// Staging.  A 4-stage LDS ring is filled with direct buffer->LDS loads
+// (buffer_load_dwordx4 ... lds: lane i of a load writes base + 16*i), so
+// several sub-blocks are in flight per workgroup without holding staging
+// registers.  For d = 128 every load fills four whole token rows and groups of
+// four rows sit 1056 bytes apart; for d = 64 rows are padded (K: 2d+16 bytes,
+// V: 2d+64 bytes).  Either way the K operand reads and the transposing V reads
+// are bank-conflict free.  Ring reads are issued in inline asm (each block
+// waits for its own results) so the compiler does not serialise them behind
+// the in-flight ring loads.  Stages are handed between waves with LDS stamps
+// and counters instead of workgroup barriers (the protocol is described at
+// the loop), so the waves sharing a SIMD drift apart and overlap one
+// another's MFMA and VALU work.
 //
-// Rows.  A row is one (query, head) pair.  Each of the NW waves owns RT fixed row tiles
-// of 16 rows (16/G queries x G heads) whose O accumulators, running max and
-// running sum stay in registers for the whole tile; for a staged sub-block a
-// wave runs MFMA only on its row tiles that contain a query which selected
-// the block, and masks the rows whose query did not (and future tokens).
+// Rows.  A row is one (query, head) pair.  Each of the NW waves owns one
+// fixed tile of 16 rows (16/G queries x G heads) whose O accumulators,
+// reference max and running sum stay in registers for the whole tile; a wave
+// visits only the sub-blocks whose block one of its queries selected, and
+// masks the rows whose query did not (and future tokens).
 //   S^T = K . Q^T     v_mfma_f32_16x16x32_bf16, A = K rows from LDS,
 //                     B = Q^T resident in registers;
-//   O^T += V^T . P^T  A = V^T read with the transposing ds_read_b64_tr_b16,
-//                     B = P^T straight from the S^T accumulators, split into
-//                     a bf16 head and tail.
+//   O^T += V^T . P^T  v_mfma_f32_16x16x32_f16, A = V^T read with the
+//                     transposing ds_read_b64_tr_b16 from an fp16 copy of V
+//                     scaled by one power of two, B = P^T (fp16) straight from
+//                     the S^T accumulators.
 // Workgroups are numbered group-fastest, so with 8 groups all tiles of a
 // group run on the same XCD and share its L2.
 #include "msa_device.h"
