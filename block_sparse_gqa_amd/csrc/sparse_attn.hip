@@ -5,15 +5,17 @@
 // selection, so one load of a K/V block serves all G heads; "MiniMax Goes
 // Sparse", section 1, step 2).
 //
-// One wave owns one (query, group).  The G heads sit on the N side of
-// v_mfma_f32_16x16x32_bf16 (padded to 16).  Per 64-token sub-block:
-//   S^T = K . Q^T   A = K rows straight from HBM (16 tokens x 16 bytes per
-//                   lane, coalesced), B = Q^T held in registers;
+// One wave owns one (split, query, group).  The G heads sit on the N side of
+// v_mfma_f32_16x16x32_bf16 (padded to 16).  Per 32-token sub-block, whose K
+// and V rows are loaded as whole lines into registers (two sub-blocks ahead)
+// and then copied to padded LDS tiles:
+//   S^T = K . Q^T   A = K rows from LDS, B = Q^T held in registers;
 //   online softmax in the exp2 domain, per head = per lane column;
 //   O^T += V^T . P^T  B = P^T comes from the S^T accumulators without any data
 //                   movement (the contraction index is permuted consistently on
-//                   both sides), A = V^T is read from a token-major LDS copy
-//                   of the V block with the transposing ds_read_b64_tr_b16.
+//                   both sides), split into a bf16 head and tail; A = V^T is
+//                   read from the token-major V tile with the transposing
+//                   ds_read_b64_tr_b16.
 // Decode splits a sequence's selected blocks over many waves and merges the
 // partial results by log-sum-exp.
 #include "msa_device.h"
