@@ -125,6 +125,52 @@ __global__ __launch_bounds__(256) void bwd_invert(const int32_t *__restrict__ id
     }
 }
 
+// Pass 0 with the counting done in LDS first: the workgroup's selections take
+// local places in an LDS histogram of all keys, then each key the workgroup
+// touched takes one block of global places with a single atomic, so popular
+// blocks see one global atomic per workgroup instead of one per selection.
+constexpr int kHistKeys = 16384;  // largest key count this path handles (64 KB of LDS)
+__global__ __launch_bounds__(256) void bwd_count_lds(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
+                                                     const int32_t *__restrict__ cu_k,
+                                                     const int32_t *__restrict__ blk_off, int num_seqs, int total_q,
+                                                     int h, int B, int top_k, int nb_max, int keys,
+                                                     int32_t *__restrict__ cnt, int32_t *__restrict__ place) {
+    extern __shared__ int hist[];  // keys entries
+    for (int x = threadIdx.x; x < keys; x += 256) hist[x] = 0;
+    __syncthreads();
+    const long pair = (long)blockIdx.x * 256 + threadIdx.x;
+    const bool live = pair < (long)total_q * h;
+    int row = 0, g = 0, s = 0, p = -1;
+    if (live) {
+        row = (int)(pair / h);
+        g = (int)(pair % h);
+        s = seq_of_row(cu_q, num_seqs, row);
+        p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
+    }
+    const int32_t *sel = ids + pair * top_k;
+    if (live) {
+        for (int a = 0; a < top_k; ++a) {
+            const int j = sel[a];
+            if (j < 0 || j > p / B) continue;
+            const int key = g * nb_max + blk_off[s] + j;
+            place[pair * top_k + a] = atomicAdd(&hist[key], 1);
+        }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < keys; x += 256) {
+        const int c = hist[x];
+        if (c > 0) hist[x] = atomicAdd(&cnt[x], c);
+    }
+    __syncthreads();
+    if (live) {
+        for (int a = 0; a < top_k; ++a) {
+            const int j = sel[a];
+            if (j < 0 || j > p / B) continue;
+            place[pair * top_k + a] += hist[g * nb_max + blk_off[s] + j];
+        }
+    }
+}
+
 // Exclusive scan of n counts into off[0..n] (one workgroup).
 __global__ __launch_bounds__(kScanThreads) void bwd_scan(const int32_t *__restrict__ cnt, long n,
                                                          int32_t *__restrict__ off) {
@@ -512,8 +558,12 @@ hipError_t launch_bwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
     hipLaunchKernelGGL((bwd_prep<D>), grid_of(rows, 4), dim3(256), 0, st, out, dout, rows, delta);
     hipLaunchKernelGGL(bwd_block_offsets, dim3(1), dim3(kScanThreads), 0, st, s.cu_k, s.num_seqs, s.B, blk_off);
     hipLaunchKernelGGL(fill_zero_i32, zgrid, dim3(256), 0, st, cnt, keys);
-    hipLaunchKernelGGL((bwd_invert<0>), grid_of(pairs, 256), dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off,
-                       s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, cnt, place, nullptr, nullptr);
+    if (keys <= kHistKeys)
+        hipLaunchKernelGGL(bwd_count_lds, grid_of(pairs, 256), dim3(256), (size_t)keys * sizeof(int), st, ids, s.cu_q, s.cu_k, blk_off,
+                           s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, (int)keys, cnt, place);
+    else
+        hipLaunchKernelGGL((bwd_invert<0>), grid_of(pairs, 256), dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off,
+                           s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, cnt, place, nullptr, nullptr);
     hipLaunchKernelGGL(bwd_scan, dim3(1), dim3(kScanThreads), 0, st, cnt, keys, off);
     hipLaunchKernelGGL((bwd_invert<1>), grid_of(pairs, 256), dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off,
                        s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, cnt, place, off, entries);

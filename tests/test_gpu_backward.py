@@ -53,6 +53,9 @@ CASES = [
     ("bwd_G16", (333,), (333,), 16, 1, 128, 64, 64, 2),
     ("bwd_dense", (257,), (257,), 8, 2, 128, 64, 64, 8),
     ("bwd_chunked", (100, 37), (300, 400), 8, 4, 128, 64, 64, 3),
+    # 16 groups x 1094 key blocks = 17504 (group, block) keys: more than the
+    # LDS histogram of the counting pass holds, so the global-atomic count runs
+    ("bwd_many_keys", (64, 64), (40000, 30000), 16, 16, 64, 32, 64, 3),
 ]
 
 
