@@ -207,6 +207,35 @@ def prefill_backward(dp, bufs, fwd, steps):
     return res
 
 
+def prefill_block_centric(dp, bufs, fwd, steps):
+    """The same prefill sparse branch on the block-centric schedule
+    (msa_sparse_attn_prefill_blocks), on the forward's own ids; its output is
+    checked against the query-tile kernel's.  Reported beside the headline."""
+    import torch
+
+    from block_sparse_gqa_amd import device, msa
+    ids, out, lse = bufs
+    ws = device._workspace(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem, dp.q.device)
+    o2, l2 = device.alloc_out(dp)
+    device.sparse_attention_blocks(dp, ids, o2, l2, ws)   # warm-up
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(steps):
+        device.sparse_attention_blocks(dp, ids, o2, l2, ws)
+    e[1].record()
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / steps
+    device.sparse_attention(dp, ids, out, lse)
+    diff = float((o2.float() - out.float()).abs().max())
+    flops = fwd["sparse_attn_TFLOP_per_s"] * fwd["sparse_attn_ms"] * 1e-3
+    res = {"ms": ms, "algorithmic_TFLOP": flops, "TFLOP_per_s": flops / (ms * 1e-3),
+           "frac_mfma_peak": flops / (ms * 1e-3) / MFMA_BF16_PEAK_TFLOPS, "workspace_GB": ws.numel() / 1e9,
+           "max_abs_diff_vs_query_tile": diff}
+    del ws, o2, l2
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +245,8 @@ def main():
     ap.add_argument("--workloads", default=",".join(WORKLOADS))
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the sparse-branch backward measurement (reported beside the headline, not in it)")
+    ap.add_argument("--no-block-centric", action="store_true",
+                    help="skip the block-centric prefill schedule measurement (reported beside the headline)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement (reported beside the headline, not in it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -331,6 +362,12 @@ def main():
                 results[name]["backward"] = prefill_backward(dps[name], bufs[name], results[name],
                                                              max(args.steps // 2, 3))
 
+    if not args.no_block_centric:
+        for name in names:
+            if not inputs[name].wl.is_decode:
+                results[name]["block_centric"] = prefill_block_centric(dps[name], bufs[name], results[name],
+                                                                       max(args.steps // 2, 3))
+
     if not args.no_paged:
         for name in names:
             if inputs[name].wl.is_decode:
@@ -348,8 +385,31 @@ def main():
     ce[1].record()
     torch.cuda.synchronize()
     copy_gbs = 2 * (1 << 32) * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
-    del src, dst
+    del dst
+    # a read-only stream of the same 4 GiB and a pure MFMA loop, from the library's own kernels
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    msa.msa_ceiling_stream_read(src, sink)
+    ce[0].record()
+    nbytes = sum(msa.msa_ceiling_stream_read(src, sink) for _ in range(5))
+    ce[1].record()
+    torch.cuda.synchronize()
+    read_gbs = nbytes / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src
+    msa.msa_ceiling_mfma_bf16(1024, sink)
+    ce[0].record()
+    flops = sum(msa.msa_ceiling_mfma_bf16(32768, sink) for _ in range(3))
+    ce[1].record()
+    torch.cuda.synchronize()
+    mfma_tfs = flops / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e12
     torch.cuda.empty_cache()
+    achievable = {"hbm": read_gbs, "mfma": mfma_tfs}
+    for r in results.values():
+        if r["bound"] == "hbm":
+            r["frac_hbm_achievable"] = r["GB_per_s"] / read_gbs
+        else:
+            r["frac_mfma_achievable"] = r["TFLOP_per_s"] / mfma_tfs
+    roofline["achievable"] = achievable[kbound]
+    roofline["frac_achievable"] = achieved / achievable[kbound]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -373,7 +433,11 @@ def main():
                    **{n: results[n]["workload"] for n in names}},
         "results": results,
         "roofline": roofline,
-        "ceilings": {"hbm_copy_GB_per_s": copy_gbs, "note": "device-to-device copy of 4 GiB, read + write bytes"},
+        "ceilings": {"hbm_copy_GB_per_s": copy_gbs, "hbm_stream_read_GB_per_s": read_gbs,
+                     "mfma_bf16_TFLOP_per_s": mfma_tfs,
+                     "note": "measured on this GPU: a device-to-device copy of 4 GiB (read + write bytes), a "
+                             "full-line read-only stream of the same 4 GiB, and back-to-back 16x16x32 bf16 MFMAs "
+                             "with no memory traffic"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

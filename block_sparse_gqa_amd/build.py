@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["msa_api.hip", "index_prefill.hip", "index_decode.hip", "topk_select.hip", "sparse_attn.hip", "attn_prefill.hip",
-           "kv_append.hip", "attn_backward.hip"]
+           "kv_append.hip", "attn_backward.hip", "block_lists.hip", "attn_block_fwd.hip",
+           "ceilings.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

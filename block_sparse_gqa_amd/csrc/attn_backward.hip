@@ -11,9 +11,7 @@
 //
 // Key-centric schedule.  dk and dv of a key block need every (query, head)
 // that selected it, so the query-centric ids are first turned into one list
-// of selecting queries per (group, block) -- the inverted index of the
-// pages' block-sparse prior art ("MoBA / FlashMoBA" page, section 3.1, its
-// third kernel) -- with counts, a scan and atomic slots (list order is not
+// of selecting queries per (group, block) (block_lists.hip; list order is not
 // fixed, so dk/dv sums are not bitwise reproducible).  One workgroup then
 // owns one (group, block): K and V of the block sit in LDS, dk and dv in
 // registers, and the selecting queries stream through in chunks of up to 32
@@ -38,16 +36,6 @@ namespace {
 
 constexpr int kRows = 32;                 // (query, head) rows per chunk
 constexpr int kRowStride = 288;           // LDS row stride of K, V, Q, dO (bytes; 32 mod 256: conflict free)
-constexpr int kScanThreads = 1024;
-
-__device__ __forceinline__ int seq_of_row(const int32_t *cu_q, int num_seqs, int row) {
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
 
 // delta[row, head] = dO . O (float32).
 template <int D>
@@ -66,139 +54,6 @@ __global__ __launch_bounds__(256) void bwd_prep(const uint16_t *__restrict__ out
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
     if (lane == 0) delta[rh] = s;
-}
-
-// blk_off[s] = number of key blocks of the sequences before s.
-__global__ __launch_bounds__(kScanThreads) void bwd_block_offsets(const int32_t *__restrict__ cu_k, int num_seqs, int B,
-                                                                 int32_t *__restrict__ blk_off) {
-    __shared__ int carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    for (int base = 0; base <= num_seqs; base += kScanThreads) {
-        const int s = base + (int)threadIdx.x;
-        const int nb = (s < num_seqs) ? (cu_k[s + 1] - cu_k[s] + B - 1) / B : 0;
-        // inclusive scan over the threads (wave scan, then across waves)
-        int x = nb;
-        const int lane = threadIdx.x & 63;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        __shared__ int wsum[kScanThreads / 64];
-        if (lane == 63) wsum[threadIdx.x >> 6] = x;
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) before += wsum[w];
-        const int c = carry;
-        if (s <= num_seqs) blk_off[s] = c + before + x - nb;
-        __syncthreads();
-        if (threadIdx.x == kScanThreads - 1) carry = c + before + x;
-        __syncthreads();
-    }
-}
-
-// Count (pass 0: each selection takes the next place of its key, kept in
-// `place`) or store (pass 1) every valid selection (row, g, block j) under key
-// g * nb_max + blk_off[s] + j; an entry is row * top_k + slot.
-template <int PASS>
-__global__ __launch_bounds__(256) void bwd_invert(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
-                                                  const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
-                                                  int num_seqs, int total_q, int h, int B, int top_k, int nb_max,
-                                                  int32_t *__restrict__ cnt, int32_t *__restrict__ place,
-                                                  const int32_t *__restrict__ off, int32_t *__restrict__ entries) {
-    const long pair = (long)blockIdx.x * 256 + threadIdx.x;
-    if (pair >= (long)total_q * h) return;
-    const int row = (int)(pair / h), g = (int)(pair % h);
-    const int s = seq_of_row(cu_q, num_seqs, row);
-    const int len_q = cu_q[s + 1] - cu_q[s], len_k = cu_k[s + 1] - cu_k[s];
-    const int p = len_k - len_q + (row - cu_q[s]);
-    const int32_t *sel = ids + pair * top_k;
-    for (int a = 0; a < top_k; ++a) {
-        const int j = sel[a];
-        if (j < 0 || j > p / B) continue;
-        const long key = (long)g * nb_max + blk_off[s] + j;
-        if (PASS == 0)
-            place[pair * top_k + a] = atomicAdd(&cnt[key], 1);
-        else
-            entries[off[key] + place[pair * top_k + a]] = row * top_k + a;
-    }
-}
-
-// Pass 0 with the counting done in LDS first: the workgroup's selections take
-// local places in an LDS histogram of all keys, then each key the workgroup
-// touched takes one block of global places with a single atomic, so popular
-// blocks see one global atomic per workgroup instead of one per selection.
-constexpr int kHistKeys = 16384;  // largest key count this path handles (64 KB of LDS)
-__global__ __launch_bounds__(256) void bwd_count_lds(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
-                                                     const int32_t *__restrict__ cu_k,
-                                                     const int32_t *__restrict__ blk_off, int num_seqs, int total_q,
-                                                     int h, int B, int top_k, int nb_max, int keys,
-                                                     int32_t *__restrict__ cnt, int32_t *__restrict__ place) {
-    extern __shared__ int hist[];  // keys entries
-    for (int x = threadIdx.x; x < keys; x += 256) hist[x] = 0;
-    __syncthreads();
-    const long pair = (long)blockIdx.x * 256 + threadIdx.x;
-    const bool live = pair < (long)total_q * h;
-    int row = 0, g = 0, s = 0, p = -1;
-    if (live) {
-        row = (int)(pair / h);
-        g = (int)(pair % h);
-        s = seq_of_row(cu_q, num_seqs, row);
-        p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
-    }
-    const int32_t *sel = ids + pair * top_k;
-    if (live) {
-        for (int a = 0; a < top_k; ++a) {
-            const int j = sel[a];
-            if (j < 0 || j > p / B) continue;
-            const int key = g * nb_max + blk_off[s] + j;
-            place[pair * top_k + a] = atomicAdd(&hist[key], 1);
-        }
-    }
-    __syncthreads();
-    for (int x = threadIdx.x; x < keys; x += 256) {
-        const int c = hist[x];
-        if (c > 0) hist[x] = atomicAdd(&cnt[x], c);
-    }
-    __syncthreads();
-    if (live) {
-        for (int a = 0; a < top_k; ++a) {
-            const int j = sel[a];
-            if (j < 0 || j > p / B) continue;
-            place[pair * top_k + a] += hist[g * nb_max + blk_off[s] + j];
-        }
-    }
-}
-
-// Exclusive scan of n counts into off[0..n] (one workgroup).
-__global__ __launch_bounds__(kScanThreads) void bwd_scan(const int32_t *__restrict__ cnt, long n,
-                                                         int32_t *__restrict__ off) {
-    __shared__ int wsum[kScanThreads / 64];
-    __shared__ int carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    for (long base = 0; base < n; base += kScanThreads) {
-        const long i = base + threadIdx.x;
-        const int v = (i < n) ? cnt[i] : 0;
-        int x = v;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        if (lane == 63) wsum[threadIdx.x >> 6] = x;
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) before += wsum[w];
-        const int c = carry;
-        if (i < n) off[i] = c + before + x - v;
-        __syncthreads();
-        if (threadIdx.x == kScanThreads - 1) carry = c + before + x;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) off[n] = carry;
 }
 
 // Transposing reads of rows r0 + 4*q4 .. +3 and r0 + 16 + 4*q4 .. +3 of a
@@ -504,36 +359,23 @@ __global__ __launch_bounds__(256) void bwd_finish(const uint16_t *__restrict__ d
                   pack_bf16x2(acc[6], acc[7])};
 }
 
+// Workspace: the block lists, then delta and the dq partials.
 struct BwdWs {
-    size_t delta, dq_part, blk_off, cnt, off, entries, place, bytes;
-    long nb_max;
+    BlockLists lists;
+    size_t delta, dq_part, bytes;
 };
 
 BwdWs bwd_ws(const Shape &s) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     BwdWs w;
-    w.nb_max = (long)s.total_k / s.B + s.num_seqs;
-    size_t at = 0;
+    w.lists = block_lists_layout(s);
+    size_t at = w.lists.bytes;
     w.delta = at;
     at += al((size_t)s.total_q * s.H * sizeof(float));
     w.dq_part = at;
     at += al((size_t)s.total_q * s.top_k * s.H * s.d * sizeof(uint16_t));
-    w.blk_off = at;
-    at += al((size_t)(s.num_seqs + 1) * sizeof(int32_t));
-    w.cnt = at;
-    at += al((size_t)s.h * w.nb_max * sizeof(int32_t));
-    w.off = at;
-    at += al(((size_t)s.h * w.nb_max + 1) * sizeof(int32_t));
-    w.entries = at;
-    at += al((size_t)s.total_q * s.h * s.top_k * sizeof(int32_t));
-    w.place = at;
-    at += al((size_t)s.total_q * s.h * s.top_k * sizeof(int32_t));
     w.bytes = at;
     return w;
-}
-
-__global__ __launch_bounds__(256) void fill_zero_i32(int32_t *__restrict__ p, long n) {
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0;
 }
 
 template <int D, int B>
@@ -544,32 +386,18 @@ hipError_t launch_bwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
     char *base = static_cast<char *>(ws);
     float *delta = reinterpret_cast<float *>(base + w.delta);
     uint16_t *dq_part = reinterpret_cast<uint16_t *>(base + w.dq_part);
-    int32_t *blk_off = reinterpret_cast<int32_t *>(base + w.blk_off);
-    int32_t *cnt = reinterpret_cast<int32_t *>(base + w.cnt);
-    int32_t *off = reinterpret_cast<int32_t *>(base + w.off);
-    int32_t *entries = reinterpret_cast<int32_t *>(base + w.entries);
-    int32_t *place = reinterpret_cast<int32_t *>(base + w.place);
+    const int32_t *blk_off = reinterpret_cast<const int32_t *>(base + w.lists.blk_off);
+    const int32_t *off = reinterpret_cast<const int32_t *>(base + w.lists.off);
+    const int32_t *entries = reinterpret_cast<const int32_t *>(base + w.lists.entries);
     const long rows = (long)s.total_q * s.H;
-    const long keys = (long)s.h * w.nb_max;
-    const long pairs = (long)s.total_q * s.h;
     auto grid_of = [](long n, long per) { return dim3((unsigned)((n + per - 1) / per)); };
-    const dim3 zgrid = grid_of(std::min(keys, 1L << 22), 256);
 
     hipLaunchKernelGGL((bwd_prep<D>), grid_of(rows, 4), dim3(256), 0, st, out, dout, rows, delta);
-    hipLaunchKernelGGL(bwd_block_offsets, dim3(1), dim3(kScanThreads), 0, st, s.cu_k, s.num_seqs, s.B, blk_off);
-    hipLaunchKernelGGL(fill_zero_i32, zgrid, dim3(256), 0, st, cnt, keys);
-    if (keys <= kHistKeys)
-        hipLaunchKernelGGL(bwd_count_lds, grid_of(pairs, 256), dim3(256), (size_t)keys * sizeof(int), st, ids, s.cu_q, s.cu_k, blk_off,
-                           s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, (int)keys, cnt, place);
-    else
-        hipLaunchKernelGGL((bwd_invert<0>), grid_of(pairs, 256), dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off,
-                           s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, cnt, place, nullptr, nullptr);
-    hipLaunchKernelGGL(bwd_scan, dim3(1), dim3(kScanThreads), 0, st, cnt, keys, off);
-    hipLaunchKernelGGL((bwd_invert<1>), grid_of(pairs, 256), dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off,
-                       s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, cnt, place, off, entries);
-    hipLaunchKernelGGL((bwd_block<D, B>), dim3((unsigned)w.nb_max, s.h), dim3(256), 0, st, q, k, v, dout, lse, delta,
-                       s.cu_q, s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.nb_max, s.top_k, scale,
-                       scale * kLog2e, dq_part, dk, dv);
+    const hipError_t e = launch_block_lists(s, ids, w.lists, base, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_block<D, B>), dim3((unsigned)w.lists.nb_max, s.h), dim3(256), 0, st, q, k, v, dout, lse,
+                       delta, s.cu_q, s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max,
+                       s.top_k, scale, scale * kLog2e, dq_part, dk, dv);
     hipLaunchKernelGGL((bwd_finish<D>), grid_of(rows, 4), dim3(256), 0, st, dq_part, ids, s.cu_q, s.cu_k, s.num_seqs,
                        rows, s.H, s.h, s.B, s.top_k, dq);
     return hipGetLastError();

@@ -1,0 +1,349 @@
+// Sparse branch, prefill, on the block-centric ("KV-outer, gather-Q")
+// schedule: the same exact softmax attention over the selected blocks as the
+// query-tile kernel ("MiniMax Goes Sparse", section 1, step 2; "MiniMax M3
+// MSA vs Step 3.7 Flash MFA", section "MSA: a minimal sparse attention",
+// second layer), computed key block by key block.  The pages name this
+// operator flow ("深度解析M3多模态模型与Token Plan", section 二.2, on
+// hardware-friendly operators) and their block-sparse prior art builds it on
+// an inverted index ("MoBA / FlashMoBA" page, section 3.1).
+//
+// Pass 1 (block_lists.hip): the ids become, per (group, key block), the list
+// of (query row, slot) pairs that selected it.
+//
+// Pass 2 (fwd_block): one workgroup per (group, block).  The block's K (bf16)
+// and V (fp16, scaled by a power of two 2^-e chosen from the block's largest
+// |v| so that every value and every partial output fits fp16) sit in LDS.
+// Each wave takes 16-row tiles of the list (16/G selecting queries x G
+// heads), gathers their Q rows straight into the MFMA B operand (two tiles
+// ahead) and computes
+//     S^T = K . Q^T         v_mfma_f32_16x16x32_bf16, A = K rows from LDS;
+//     P   = 2^(S c2 - m)    m = the row's max over the block's visible tokens;
+//     O^T = V^T . P^T       v_mfma_f32_16x16x32_f16, A = V^T (transposing LDS
+//                           read), B = P^T straight from the S^T accumulators.
+// Every (row, slot, head) gets a partial: O / l as fp16 (times 2^-e) and the
+// pair (m + log2 l, e), the partial rows staged through a per-wave LDS tile
+// so that stores cover whole rows.  No workgroup barrier after the staging:
+// each wave walks its own tiles, with the list entries three tiles ahead and
+// the Q rows two tiles ahead in registers.
+//
+// Pass 3 (fwd_merge): per (row, head), the partials of the row's valid slots
+// merge by log-sum-exp into O (bf16) and LSE (natural log), summed in slot
+// order.
+#include <algorithm>
+
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kStride = 288;   // LDS row stride of K and V in bytes (32 mod 256: conflict free)
+
+// Row r of a row-major 16-bit tile, 8 values at column 8 * c8.
+__device__ __forceinline__ uint4 lds_row8(const char *tile, int r, int c8) {
+    return *reinterpret_cast<const uint4 *>(tile + r * kStride + 16 * c8);
+}
+
+// Transposing reads of rows r0 + 4*q4 .. +3 and r0 + 16 + 4*q4 .. +3 of a
+// row-major 16-bit tile, column 16*ct + (lane % 16): an MFMA operand whose k
+// slots 8*q4 + i are those rows.
+__device__ __forceinline__ uint4 lds_tr_rows(const char *tile, int r0, int ct) {
+    const int lane = lane_id(), l16 = lane & 15, q4 = lane >> 4;
+    const char *p = tile + (r0 + 4 * q4 + (l16 >> 2)) * kStride + 8 * (l16 & 3) + 32 * ct;
+    const uint2 x = __builtin_bit_cast(uint2, lds_read_tr16(p));
+    const uint2 y = __builtin_bit_cast(uint2, lds_read_tr16(p + 16 * kStride));
+    return uint4{x.x, x.y, y.x, y.y};
+}
+
+// Waves per workgroup: B = 128 keeps two waves per SIMD with one workgroup
+// per CU (its K/V tiles take 72 KB of LDS).
+template <int B>
+constexpr int fwd_waves() { return B == 128 ? 8 : 4; }
+
+template <int D, int B>
+__global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
+    const int32_t *__restrict__ off, const int32_t *__restrict__ entries, int num_seqs, int H, int h, int nb_max,
+    int top_k, float c2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_w) {
+    constexpr int KS = D / 32;            // 32-wide k steps over d
+    constexpr int DT = D / 16;            // 16-wide d tiles
+    constexpr int TT = B / 16;            // 16-token tiles of the block
+    constexpr int NW = fwd_waves<B>();
+    constexpr int NT = 64 * NW;
+    constexpr int CH = B * (D / 8) / NT;  // 16-byte chunks per thread per tensor
+    constexpr int OSTR = 2 * D + 16;      // LDS row stride of a wave's output tile
+    __shared__ __attribute__((aligned(16))) char kt[B * kStride];
+    __shared__ __attribute__((aligned(16))) char vt[B * kStride];
+    __shared__ __attribute__((aligned(16))) char ot[NW][16 * OSTR];
+    __shared__ uint32_t vmax_bits;
+
+    const int gb = blockIdx.x, g = blockIdx.y;
+    if (gb >= blk_off[num_seqs]) return;
+    const int s = seq_of_row(blk_off, num_seqs, gb);
+    const int j = gb - blk_off[s];
+    const long key = (long)g * nb_max + gb;
+    const int e0 = off[key], nq = off[key + 1] - e0;
+    if (nq == 0) return;
+    const int k_begin = cu_k[s], len_k = cu_k[s + 1] - k_begin;
+    const int q_begin = cu_q[s], shift = len_k - (cu_q[s + 1] - q_begin);
+    const int G = H / h, qpt = 16 / G, rows_used = qpt * G;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int t_valid = min(B, len_k - j * B);   // tokens of the block inside the sequence
+
+    // Stage K (bf16) and V (fp16 x 2^-e); rows past the sequence end are zero.
+    if (tid == 0) vmax_bits = 0u;
+    uint4 kr[CH], vr[CH];
+    uint32_t vmax = 0u;
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int c = x * NT + tid, t = c / (D / 8), c8 = c % (D / 8);
+        const size_t src = ((size_t)(k_begin + j * B + min(t, t_valid - 1)) * h + g) * D + c8 * 8;
+        kr[x] = load16(k + src);
+        vr[x] = load16(v + src);
+        const uint32_t m = t < t_valid ? 0xffffffffu : 0u;   // per-word mask
+        kr[x] = uint4{kr[x].x & m, kr[x].y & m, kr[x].z & m, kr[x].w & m};
+        vr[x] = uint4{vr[x].x & m, vr[x].y & m, vr[x].z & m, vr[x].w & m};
+        const uint32_t w[4] = {vr[x].x, vr[x].y, vr[x].z, vr[x].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vmax = max(vmax, max((w[i] & 0x7fffu) << 16, w[i] & 0x7fff0000u));   // |v| bits
+    }
+    __syncthreads();
+    atomicMax(&vmax_bits, vmax);
+    __syncthreads();
+    // 2^-e brings the largest |v| into [2^14, 2^15): v and O / l fit fp16.
+    const uint32_t amax = vmax_bits;
+    const int e = amax == 0u ? 0 : min(max((int)(amax >> 23) - 127 - 14, -100), 113);
+    const float vscale = __uint_as_float((uint32_t)(127 - e) << 23);
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int c = x * NT + tid, t = c / (D / 8), c8 = c % (D / 8);
+        *reinterpret_cast<uint4 *>(kt + t * kStride + 16 * c8) = kr[x];
+        const uint32_t w[4] = {vr[x].x, vr[x].y, vr[x].z, vr[x].w};
+        uint32_t f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f[i] = pack_f16x2(__uint_as_float(w[i] << 16) * vscale, __uint_as_float(w[i] & 0xffff0000u) * vscale);
+        *reinterpret_cast<uint4 *>(vt + t * kStride + 16 * c8) = uint4{f[0], f[1], f[2], f[3]};
+    }
+    __syncthreads();
+
+    // This lane's row of a tile: query l16 / G of the tile, head g*G + l16 % G.
+    const int qi = l16 / G, hd = l16 % G;
+    const int ntiles = (nq + qpt - 1) / qpt;
+    auto entry = [&](int t) {   // row * top_k + slot, or -1
+        const int x = t * qpt + qi;
+        return (t < ntiles && l16 < rows_used && x < nq) ? entries[e0 + x] : -1;
+    };
+    auto load_q = [&](uint4 (&qo)[KS], int ent) {   // row 0 stands in for unused lanes
+        const size_t base = ((size_t)(ent >= 0 ? ent / top_k : 0) * H + g * G + hd) * D + 8 * q4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qo[ks] = load16(q + base + 32 * ks);
+    };
+
+    int t = wave;
+    int ent_cur = entry(t), ent_next = entry(t + NW), ent_n2 = entry(t + 2 * NW);
+    uint4 qc[KS], qn[KS] = {}, qn2[KS] = {};
+    load_q(qc, ent_cur);
+    if (t + NW < ntiles) load_q(qn, ent_next);
+    for (; t < ntiles; t += NW) {
+        const int ent_after = entry(t + 3 * NW);
+        if (t + 2 * NW < ntiles) load_q(qn2, ent_n2);
+
+        f32x4 sa[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            sa[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sa[tt] = mfma16x16x32(as_bf16x8(lds_row8(kt, 16 * tt + l16, 4 * ks + q4)), as_bf16x8(qc[ks]), sa[tt]);
+        }
+        // Visible tokens of this lane's row: block token index <= lim.
+        const int row = ent_cur >= 0 ? ent_cur / top_k : -1;
+        const int lim = row >= 0 ? shift + (row - q_begin) - j * B : -1;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = 16 * tt + 4 * q4 + i <= lim ? sa[tt][i] * c2 : -INFINITY;
+                sa[tt][i] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = max_xor32(max_xor16(mx));
+        const float mu = mx == -INFINITY ? 0.f : mx;
+        float lsum = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(sa[tt][i] - mu);
+                sa[tt][i] = p;
+                lsum += p;
+            }
+        lsum = sum_xor32(sum_xor16(lsum));
+
+        f32x4 oa[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s32 = 0; s32 < B / 32; ++s32) {
+            // B = P^T: k slot 8*q4 + i <- token 32*s32 + 4*q4 + i, slot 8*q4 + 4 + i <- token 32*s32 + 16 + 4*q4 + i
+            const f16x8 pb = as_f16x8(uint4{pack_f16x2(sa[2 * s32][0], sa[2 * s32][1]),
+                                            pack_f16x2(sa[2 * s32][2], sa[2 * s32][3]),
+                                            pack_f16x2(sa[2 * s32 + 1][0], sa[2 * s32 + 1][1]),
+                                            pack_f16x2(sa[2 * s32 + 1][2], sa[2 * s32 + 1][3])});
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                oa[dt] = mfma16x16x32_f16(as_f16x8(lds_tr_rows(vt, 32 * s32, dt)), pb, oa[dt]);
+        }
+        // O / l (fp16) goes through this wave's LDS tile so that every store
+        // instruction writes whole partial rows (16 lanes x 16 bytes per row
+        // for d = 128).
+        const float inv = row >= 0 ? 1.0f / lsum : 0.f;
+        char *my = ot[wave];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<uint2 *>(my + l16 * OSTR + (16 * dt + 4 * q4) * 2) =
+                uint2{pack_f16x2(oa[dt][0] * inv, oa[dt][1] * inv), pack_f16x2(oa[dt][2] * inv, oa[dt][3] * inv)};
+        wave_lds_sync();
+        constexpr int CPR = D / 8;      // 16-byte chunks per row
+        constexpr int RPI = 64 / CPR;   // rows per store instruction
+#pragma unroll
+        for (int x = 0; x < 16 / RPI; ++x) {
+            const int r = x * RPI + lane / CPR, c = lane % CPR;
+            const int er = __shfl(ent_cur, r, 64);   // the entry of tile row r (held by lane r)
+            const uint4 val = *reinterpret_cast<const uint4 *>(my + r * OSTR + 16 * c);
+            if (er >= 0) *reinterpret_cast<uint4 *>(part_o + ((size_t)er * H + g * G + r % G) * D + 8 * c) = val;
+        }
+        if (row >= 0 && q4 == 0)
+            part_w[(size_t)ent_cur * H + g * G + hd] = make_float2(mu + __log2f(lsum), (float)e);
+        ent_cur = ent_next;
+        ent_next = ent_n2;
+        ent_n2 = ent_after;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qc[ks] = qn[ks];
+            qn[ks] = qn2[ks];
+        }
+    }
+}
+
+// O[row, head] and LSE from the partials of the row's valid slots.  One wave
+// per (row, head); lane = (slot lane group, 16-byte chunk of a partial row),
+// so every load instruction reads whole partial rows.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ part_o, const float2 *__restrict__ part_w,
+                                                 const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
+                                                 const int32_t *__restrict__ cu_k, int num_seqs, long n_rows, int H,
+                                                 int h, int B, int top_k, uint16_t *__restrict__ out,
+                                                 float *__restrict__ lse) {
+    constexpr int CPR = D / 8;       // 16-byte chunks per partial row
+    constexpr int NSO = 64 / CPR;    // slot lane groups
+    const long rh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rh >= n_rows) return;
+    const int lane = threadIdx.x & 63, c = lane % CPR, so = lane / CPR;
+    const int row = (int)(rh / H), head = (int)(rh % H), g = head / (H / h);
+    const int s = seq_of_row(cu_q, num_seqs, row);
+    const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
+    const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
+    const size_t base = (size_t)row * top_k;
+
+    float m = -INFINITY;
+    for (int a = lane; a < top_k; a += 64) {
+        const int j = sel[a];
+        if (j >= 0 && j <= p / B) m = fmaxf(m, part_w[(base + a) * H + head].x);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float mu = m == -INFINITY ? 0.f : m;
+
+    float acc[8], den = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 4
+    for (int a = so; a < top_k; a += NSO) {
+        const int j = sel[a];
+        const bool ok = j >= 0 && j <= p / B;
+        const size_t sh = (base + (ok ? a : 0)) * H + head;
+        const float2 w = part_w[sh];
+        const uint4 x = load16(part_o + sh * D + 8 * c);
+        const float wn = ok ? fast_exp2(w.x - mu + w.y) : 0.f;   // weight of the stored (scaled) partial
+        const float wd = ok ? fast_exp2(w.x - mu) : 0.f;
+        const f16x8 hv = as_f16x8(x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += ok ? wn * (float)hv[i] : 0.f;   // skipped slots hold no partial
+        den += c == 0 ? wd : 0.f;
+    }
+#pragma unroll
+    for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o, 64);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o, 64);
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    if (so == 0)
+        *reinterpret_cast<uint4 *>(out + (size_t)rh * D + 8 * c) =
+            uint4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                  pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    if (lse != nullptr && lane == 0) lse[rh] = den > 0.f ? (mu + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+}
+
+struct FwdWs {
+    BlockLists lists;
+    size_t part_o, part_w, bytes;
+};
+
+FwdWs fwd_ws(const Shape &s) {
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    FwdWs w;
+    w.lists = block_lists_layout(s);
+    size_t at = w.lists.bytes;
+    w.part_o = at;
+    at += al((size_t)s.total_q * s.top_k * s.H * s.d * sizeof(uint16_t));
+    w.part_w = at;
+    at += al((size_t)s.total_q * s.top_k * s.H * sizeof(float2));
+    w.bytes = at;
+    return w;
+}
+
+template <int D, int B>
+hipError_t launch_fwd(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *ids,
+                      float scale, uint16_t *out, float *lse, void *ws, hipStream_t st) {
+    const FwdWs w = fwd_ws(s);
+    char *base = static_cast<char *>(ws);
+    const int32_t *blk_off = reinterpret_cast<const int32_t *>(base + w.lists.blk_off);
+    const int32_t *off = reinterpret_cast<const int32_t *>(base + w.lists.off);
+    const int32_t *entries = reinterpret_cast<const int32_t *>(base + w.lists.entries);
+    uint16_t *part_o = reinterpret_cast<uint16_t *>(base + w.part_o);
+    float2 *part_w = reinterpret_cast<float2 *>(base + w.part_w);
+    const hipError_t e = launch_block_lists(s, ids, w.lists, base, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_block<D, B>), dim3((unsigned)w.lists.nb_max, s.h), dim3(64 * fwd_waves<B>()), 0, st, q, k, v, s.cu_q,
+                       s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max, s.top_k,
+                       scale * kLog2e, part_o, part_w);
+    const long rows = (long)s.total_q * s.H;
+    hipLaunchKernelGGL((fwd_merge<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, part_o, part_w, ids, s.cu_q,
+                       s.cu_k, s.num_seqs, rows, s.H, s.h, s.B, s.top_k, out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t block_prefill_workspace_bytes(const Shape &s) { return fwd_ws(s).bytes; }
+
+hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                      const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
+                                      hipStream_t st) {
+    if (s.H / s.h > 16) return hipErrorInvalidValue;
+    if ((long)s.total_q * s.top_k > 0x7fffffffL) return hipErrorInvalidValue;   // entries are row * top_k + slot
+    if (s.d == 64 && s.B == 64) return launch_fwd<64, 64>(s, q, k, v, ids, scale, out, lse, ws, st);
+    if (s.d == 64 && s.B == 128) return launch_fwd<64, 128>(s, q, k, v, ids, scale, out, lse, ws, st);
+    if (s.d == 128 && s.B == 64) return launch_fwd<128, 64>(s, q, k, v, ids, scale, out, lse, ws, st);
+    if (s.d == 128 && s.B == 128) return launch_fwd<128, 128>(s, q, k, v, ids, scale, out, lse, ws, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace msa

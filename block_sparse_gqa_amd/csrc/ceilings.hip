@@ -1,0 +1,82 @@
+// Achievable ceilings of this GPU, measured with the same toolchain as the
+// method's kernels, so that each kernel's rate can be set against what the
+// part really delivers as well as against its published peaks.
+//
+//  * stream_read: every byte of a buffer read once, nothing written.  Each
+//    load instruction of a wave reads one contiguous 1 KB run (lane i takes
+//    its i-th 16-byte chunk), eight runs in flight per wave, and consecutive
+//    waves take consecutive runs, which is the access pattern of the decode
+//    index scan.
+//  * mfma_bf16: back-to-back v_mfma_f32_16x16x32_bf16 on eight independent
+//    accumulators per wave (so no product waits for the previous one), two
+//    waves per SIMD, no memory traffic.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kRuns = 8;                     // 1 KB runs per wave per iteration
+constexpr int kChunksPerIter = kRuns * 64;   // 16-byte chunks per wave per iteration
+
+__global__ __launch_bounds__(256) void stream_read(const uint4 *__restrict__ p, long long iters,
+                                                   uint32_t *__restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long nwaves = (long long)gridDim.x * 4;
+    uint32_t acc = 0;
+    for (long long i = 0; i < iters; ++i) {
+        const uint4 *base = p + (i * nwaves + wave) * kChunksPerIter + lane;
+        uint4 r[kRuns];
+#pragma unroll
+        for (int u = 0; u < kRuns; ++u) r[u] = base[u * 64];
+#pragma unroll
+        for (int u = 0; u < kRuns; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+    }
+    // The xor of the data decides whether anything is stored, so no load can
+    // be dropped; the store itself almost never happens.
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+constexpr int kChains = 8;
+
+__global__ __launch_bounds__(256) void mfma_loop(int iters, float *__restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t w = 0x3c003c00u + (uint32_t)lane;   // small, finite bf16 pairs
+    const bf16x8 a = as_bf16x8(uint4{w, w ^ 1u, w ^ 2u, w ^ 3u});
+    const bf16x8 b = as_bf16x8(uint4{w ^ 4u, w ^ 5u, w ^ 6u, w ^ 7u});
+    f32x4 c[kChains];
+#pragma unroll
+    for (int u = 0; u < kChains; ++u) c[u] = f32x4{(float)u, 0.f, 0.f, (float)lane};
+    // Each product accumulates in place (dst = srcC), written in asm: with the
+    // builtin the compiler shuffles the loop-carried accumulators between
+    // registers on every iteration, which the loop would then measure.
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int u = 0; u < kChains; ++u)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[u]) : "v"(a), "v"(b));
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < kChains; ++u) s += c[u][0] + c[u][1] + c[u][2] + c[u][3];
+    if (s == 1234.5f) sink[0] = s;
+}
+
+}  // namespace
+
+long long stream_read_bytes_per_iter(int num_cus) { return (long long)num_cus * 8 * 4 * kChunksPerIter * 16; }
+
+hipError_t launch_stream_read(const void *buf, long long iters, int num_cus, uint32_t *sink, hipStream_t st) {
+    hipLaunchKernelGGL(stream_read, dim3(num_cus * 8), dim3(256), 0, st, reinterpret_cast<const uint4 *>(buf), iters,
+                       sink);
+    return hipGetLastError();
+}
+
+double mfma_loop_flops(int num_cus, int iters) { return (double)num_cus * 2 * 4 * iters * kChains * (16.0 * 16 * 32 * 2); }
+
+hipError_t launch_mfma_loop(int iters, int num_cus, float *sink, hipStream_t st) {
+    hipLaunchKernelGGL(mfma_loop, dim3(num_cus * 2), dim3(256), 0, st, iters, sink);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -110,6 +110,9 @@ size_t msa_workspace_size(int op, const msa_problem_t *problem) {
         case MSA_OP_SPARSE_ATTN_BACKWARD:
             if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
             return msa::backward_workspace_bytes(to_shape(p));
+        case MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS:
+            if (attn_support(p) != MSA_SUCCESS || p.num_heads / p.num_kv_heads > 16) return (size_t)-1;
+            return msa::block_prefill_workspace_bytes(to_shape(p));
     }
     return (size_t)-1;
 }
@@ -135,6 +138,26 @@ msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf1
     if ((st = check_ws(workspace, workspace_bytes, msa::prefill_workspace_bytes(s))) != MSA_SUCCESS) return st;
     return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+msa_status_t msa_sparse_attn_prefill_blocks(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
+                                            const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
+                                            msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
+                                            msa_stream_t stream) {
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if (q == nullptr || k == nullptr || v == nullptr || topk_ids == nullptr || out == nullptr)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
+    if ((st = attn_support(p)) != MSA_SUCCESS) return st;
+    if (p.num_heads / p.num_kv_heads > 16) return MSA_ERROR_NOT_SUPPORTED;
+    if ((long long)p.total_q * p.top_k > 0x7fffffffLL) return MSA_ERROR_NOT_SUPPORTED;
+    Shape s = to_shape(p);
+    if ((st = check_ws(workspace, workspace_bytes, msa::block_prefill_workspace_bytes(s))) != MSA_SUCCESS) return st;
+    return launched(msa::launch_attn_prefill_blocks(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
+                                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
 msa_status_t msa_sparse_attn_prefill_backward(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
@@ -269,6 +292,36 @@ msa_status_t msa_kv_append_paged(int32_t num_tokens, int32_t num_kv_heads, int32
     return launched(msa::launch_kv_append(num_tokens, num_kv_heads, head_dim, index_dim, (long long)pool_rows,
                                           slot_mapping, k, v, k_idx, k_pool, v_pool, k_idx_pool,
                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+namespace {
+int current_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+}  // namespace
+
+msa_status_t msa_ceiling_stream_read(const void *buffer, size_t buffer_bytes, uint32_t *sink, size_t *bytes_read,
+                                     msa_stream_t stream) {
+    if (buffer == nullptr || sink == nullptr || bytes_read == nullptr) return MSA_ERROR_INVALID_VALUE;
+    if ((reinterpret_cast<uintptr_t>(buffer) & 15u) != 0) return MSA_ERROR_INVALID_VALUE;
+    const int cus = current_cu_count();
+    if (cus < 1) return MSA_ERROR_LAUNCH;
+    const long long per = msa::stream_read_bytes_per_iter(cus);
+    const long long iters = (long long)(buffer_bytes / (size_t)per);
+    if (iters < 1) return MSA_ERROR_INVALID_VALUE;
+    *bytes_read = (size_t)(iters * per);
+    return launched(msa::launch_stream_read(buffer, iters, cus, sink, reinterpret_cast<hipStream_t>(stream)));
+}
+
+msa_status_t msa_ceiling_mfma_bf16(int32_t iterations, float *sink, double *flops, msa_stream_t stream) {
+    if (iterations < 1 || sink == nullptr || flops == nullptr) return MSA_ERROR_INVALID_VALUE;
+    const int cus = current_cu_count();
+    if (cus < 1) return MSA_ERROR_LAUNCH;
+    *flops = msa::mfma_loop_flops(cus, iterations);
+    return launched(msa::launch_mfma_loop(iterations, cus, sink, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -126,4 +126,15 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// Sequence of a packed row: the last s with cu[s] <= row (binary search over
+// the num_seqs + 1 prefix offsets).
+__device__ __forceinline__ int seq_of_row(const int32_t *cu, int num_seqs, int row) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
 }  // namespace msa

@@ -40,10 +40,32 @@ size_t prefill_workspace_bytes(const Shape &s);
 hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                hipStream_t st);
+// The same attention on the block-centric schedule (lists, per-block
+// partials, log-sum-exp merge).
+size_t block_prefill_workspace_bytes(const Shape &s);
+hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                      const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
+                                      hipStream_t st);
 // Copy new K/V/K_idx rows into paged pools at the given pool rows.
 hipError_t launch_kv_append(int n, int h, int d, int d_idx, long long pool_rows, const int32_t *slots,
                             const uint16_t *k, const uint16_t *v, const uint16_t *k_idx, uint16_t *k_pool,
                             uint16_t *v_pool, uint16_t *k_idx_pool, hipStream_t st);
+// Ceilings: a streaming read of the whole buffer in iterations of
+// stream_read_bytes_per_iter bytes, and a pure MFMA loop.
+long long stream_read_bytes_per_iter(int num_cus);
+hipError_t launch_stream_read(const void *buf, long long iters, int num_cus, uint32_t *sink, hipStream_t st);
+double mfma_loop_flops(int num_cus, int iters);
+hipError_t launch_mfma_loop(int iters, int num_cus, float *sink, hipStream_t st);
+// Inverted index of a prefill selection (byte offsets into one workspace):
+// per key g * nb_max + blk_off[s] + j, the entries row * top_k + slot of the
+// selections holding block j of sequence s in group g, in
+// entries[off[key] .. off[key + 1]).
+struct BlockLists {
+    size_t blk_off, cnt, off, entries, place, bytes;
+    long nb_max;
+};
+BlockLists block_lists_layout(const Shape &s);
+hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLists &w, char *base, hipStream_t st);
 // Backward of the sparse branch (prefill, selection fixed).
 size_t backward_workspace_bytes(const Shape &s);
 hipError_t launch_attn_backward(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,

@@ -25,6 +25,7 @@ MSA_OP_INDEX_TOPK = 0
 MSA_OP_SPARSE_ATTN_PREFILL = 1
 MSA_OP_SPARSE_ATTN_DECODE = 2
 MSA_OP_SPARSE_ATTN_BACKWARD = 3
+MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS = 4
 
 SIZE_MAX = (1 << 64) - 1
 
@@ -85,6 +86,8 @@ def load():
     lib.msa_index_topk.restype = ctypes.c_int
     lib.msa_sparse_attn_prefill.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
     lib.msa_sparse_attn_prefill.restype = ctypes.c_int
+    lib.msa_sparse_attn_prefill_blocks.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
+    lib.msa_sparse_attn_prefill_blocks.restype = ctypes.c_int
     lib.msa_sparse_attn_decode.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
     lib.msa_sparse_attn_decode.restype = ctypes.c_int
     paged = ctypes.POINTER(msa_paged_kv_t)
@@ -99,6 +102,10 @@ def load():
     lib.msa_kv_append_paged.restype = ctypes.c_int
     lib.msa_sparse_attn_prefill_backward.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, S, P]
     lib.msa_sparse_attn_prefill_backward.restype = ctypes.c_int
+    lib.msa_ceiling_stream_read.argtypes = [P, S, P, ctypes.POINTER(S), P]
+    lib.msa_ceiling_stream_read.restype = ctypes.c_int
+    lib.msa_ceiling_mfma_bf16.argtypes = [i32, P, ctypes.POINTER(ctypes.c_double), P]
+    lib.msa_ceiling_mfma_bf16.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [ctypes.c_int, prob]
     lib.msa_workspace_size.restype = S
     lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -179,6 +186,13 @@ def msa_sparse_attn_prefill(problem, q, k, v, topk_ids, softmax_scale, out, lse=
                                           _nbytes(workspace), _stream(stream)), "msa_sparse_attn_prefill")
 
 
+def msa_sparse_attn_prefill_blocks(problem, q, k, v, topk_ids, softmax_scale, out, lse=None, workspace=None,
+                                   stream=None):
+    _check(load().msa_sparse_attn_prefill_blocks(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_ids),
+                                                 float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                                 _nbytes(workspace), _stream(stream)), "msa_sparse_attn_prefill_blocks")
+
+
 def msa_sparse_attn_decode(problem, q, k_cache, v_cache, topk_ids, softmax_scale, out, lse=None, workspace=None,
                            stream=None):
     _check(load().msa_sparse_attn_decode(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -234,3 +248,19 @@ def msa_sparse_attn_prefill_backward(problem, q, k, v, topk_ids, softmax_scale, 
                                                    float(softmax_scale), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
                                                    _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
                                                    _stream(stream)), "msa_sparse_attn_prefill_backward")
+
+
+def msa_ceiling_stream_read(buffer, sink, stream=None):
+    """Launch one full read of `buffer` (a device tensor); returns the bytes the launch reads."""
+    n = ctypes.c_size_t(0)
+    _check(load().msa_ceiling_stream_read(_ptr(buffer), _nbytes(buffer), _ptr(sink), ctypes.byref(n), _stream(stream)),
+           "msa_ceiling_stream_read")
+    return int(n.value)
+
+
+def msa_ceiling_mfma_bf16(iterations, sink, stream=None):
+    """Launch the pure MFMA loop; returns the flops of the launch."""
+    f = ctypes.c_double(0.0)
+    _check(load().msa_ceiling_mfma_bf16(int(iterations), _ptr(sink), ctypes.byref(f), _stream(stream)),
+           "msa_ceiling_mfma_bf16")
+    return float(f.value)

@@ -63,7 +63,8 @@ typedef enum {
     MSA_OP_INDEX_TOPK = 0,
     MSA_OP_SPARSE_ATTN_PREFILL = 1,
     MSA_OP_SPARSE_ATTN_DECODE = 2,
-    MSA_OP_SPARSE_ATTN_BACKWARD = 3
+    MSA_OP_SPARSE_ATTN_BACKWARD = 3,
+    MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS = 4
 } msa_op_t;
 
 typedef struct {
@@ -150,6 +151,29 @@ msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16
                                     const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out,
                                     float *lse, void *workspace, size_t workspace_bytes,
                                     msa_stream_t stream);
+
+/*
+ * msa_sparse_attn_prefill on the block-centric ("KV-outer, gather-Q")
+ * schedule: the same result, computed key block by key block.  The pages
+ * name this operator flow ("深度解析M3多模态模型与Token Plan", section 二.2)
+ * and their block-sparse prior art turns query-centric selections into
+ * per-block lists of queries for it ("MoBA / FlashMoBA" page, section 3.1).
+ * Each (group, block) of K/V is read once; each (row, selected slot, head)
+ * leaves a normalised partial output that a last pass merges by
+ * log-sum-exp.
+ *
+ * Arguments, layouts and errors as for msa_sparse_attn_prefill.
+ * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS)
+ * bytes, 16-byte aligned: the per-(group, block) lists and one fp16 partial
+ * per (row, selected slot, head) -- total_q * top_k * H * (2 d + 8) bytes, the
+ * bulk of it (8.7 GB for 32K tokens, 32 heads, k = 32).  Results are
+ * reproducible bit for bit (each row's partials merge in slot order).  Needs
+ * H/h <= 16 and total_q * top_k < 2^31 (MSA_ERROR_NOT_SUPPORTED otherwise).
+ */
+msa_status_t msa_sparse_attn_prefill_blocks(const msa_problem_t *problem, const msa_bf16_t *q,
+                                            const msa_bf16_t *k, const msa_bf16_t *v, const int32_t *topk_ids,
+                                            float softmax_scale, msa_bf16_t *out, float *lse, void *workspace,
+                                            size_t workspace_bytes, msa_stream_t stream);
 
 /*
  * Backward of the sparse branch, prefill, with the selection held fixed (the
@@ -265,6 +289,30 @@ typedef struct {
 msa_status_t msa_index_topk_ex(const msa_problem_t *problem, const msa_select_options_t *options,
                                const msa_paged_kv_t *paged, const msa_bf16_t *q_idx, const msa_bf16_t *k_idx,
                                int32_t *topk_ids, void *workspace, size_t workspace_bytes, msa_stream_t stream);
+
+/*
+ * Measurement helpers, not part of the method: the achievable ceilings that
+ * the method's kernels are compared with, next to the published peaks.
+ *
+ * msa_ceiling_stream_read reads the first *bytes_read bytes of `buffer`
+ * (device, 16-byte aligned) once with full-line loads and writes nothing but,
+ * in the rarest case, one word of `sink` (device, 4 bytes).  *bytes_read
+ * (host) is set before the launch to the largest multiple of the per-launch
+ * stride (256 KB per compute unit) that fits in buffer_bytes; a buffer smaller
+ * than one stride is rejected.
+ *
+ * msa_ceiling_mfma_bf16 runs `iterations` rounds of eight independent
+ * v_mfma_f32_16x16x32_bf16 per wave, two waves per SIMD on every compute
+ * unit, with no memory traffic; *flops (host) is set before the launch to the
+ * multiply-add work of the launch (2 flop each).  `sink` (device, 4 bytes)
+ * is written only in the rarest case.
+ *
+ * Both use the current device's compute-unit count and are asynchronous on
+ * `stream`; time them with events on that stream.
+ */
+msa_status_t msa_ceiling_stream_read(const void *buffer, size_t buffer_bytes, uint32_t *sink, size_t *bytes_read,
+                                     msa_stream_t stream);
+msa_status_t msa_ceiling_mfma_bf16(int32_t iterations, float *sink, double *flops, msa_stream_t stream);
 
 /* Workspace bytes an entry point needs for `problem` (0 if none).  Returns
  * (size_t)-1 when the problem is invalid or unsupported for that op. */

@@ -217,3 +217,34 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(msa, "LIB_PATH", str(tmp_path / "libmsa.so"))
     with pytest.raises(RuntimeError, match="missing"):
         msa.load()
+
+
+def test_ceilings_reject(lib):
+    n = ctypes.c_size_t(0)
+    f = ctypes.c_double(0.0)
+    read, mfma = lib.msa_ceiling_stream_read, lib.msa_ceiling_mfma_bf16
+    assert read(None, 1 << 30, FAKE, ctypes.byref(n), None) == msa.MSA_ERROR_INVALID_VALUE
+    assert read(FAKE, 1 << 30, None, ctypes.byref(n), None) == msa.MSA_ERROR_INVALID_VALUE
+    assert read(FAKE, 1 << 30, FAKE, None, None) == msa.MSA_ERROR_INVALID_VALUE
+    assert read(FAKE + 4, 1 << 30, FAKE, ctypes.byref(n), None) == msa.MSA_ERROR_INVALID_VALUE
+    assert mfma(0, FAKE, ctypes.byref(f), None) == msa.MSA_ERROR_INVALID_VALUE
+    assert mfma(16, None, ctypes.byref(f), None) == msa.MSA_ERROR_INVALID_VALUE
+    assert mfma(16, FAKE, None, None) == msa.MSA_ERROR_INVALID_VALUE
+
+
+def test_block_prefill_rejects(lib):
+    blk = lib.msa_sparse_attn_prefill_blocks
+    p = prob()
+    need = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(p))
+    # lists + one fp16 partial row and its (lse, exponent) pair per (row, slot, head)
+    assert need >= 128 * 4 * 8 * (2 * 128 + 8)
+    assert attn_call(lib, blk, prob(head_dim=96)) == msa.MSA_ERROR_NOT_SUPPORTED
+    assert attn_call(lib, blk, prob(num_heads=34, num_kv_heads=2)) == msa.MSA_ERROR_NOT_SUPPORTED   # G = 17
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS,
+                                  ctypes.byref(prob(num_heads=34, num_kv_heads=2))) == msa.SIZE_MAX
+    assert attn_call(lib, blk, prob(), q=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert attn_call(lib, blk, prob(), out=None) == msa.MSA_ERROR_INVALID_VALUE
+    assert attn_call(lib, blk, prob(), scale=-1.0) == msa.MSA_ERROR_INVALID_VALUE
+    assert attn_call(lib, blk, prob(), ws=None) == msa.MSA_ERROR_WORKSPACE
+    assert attn_call(lib, blk, prob(), ws=FAKE, ws_bytes=need - 1) == msa.MSA_ERROR_WORKSPACE
+    assert attn_call(lib, blk, prob(total_q=0, max_seqlen_q=0), q=None) == msa.MSA_SUCCESS
