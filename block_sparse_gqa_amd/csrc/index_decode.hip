@@ -140,9 +140,10 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
 
 template <int DI, int B>
 hipError_t launch(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx, float *scores, hipStream_t st) {
-    // about 2048 workgroups in all, each wave taking every nwaves-th block
+    // about 4096 workgroups in all, each wave taking every nwaves-th block
+    // (1M context: 109 us against 111 us with 2048 and 114 us with 1024 or 8192)
     const int e_max = (s.max_k + s.B - 1) / s.B;
-    int per_seq = (2048 + s.num_seqs - 1) / s.num_seqs;
+    int per_seq = (4096 + s.num_seqs - 1) / s.num_seqs;
     const int need = (e_max + kWaves - 1) / kWaves;
     if (per_seq > need) per_seq = need;
     dim3 grid(per_seq, s.num_seqs);
