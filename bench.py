@@ -235,31 +235,41 @@ def prefill_backward(dp, bufs, fwd, steps):
     return res
 
 
-def prefill_block_centric(dp, bufs, fwd, steps):
-    """The same prefill sparse branch on the block-centric schedule
-    (msa_sparse_attn_prefill_blocks), on the forward's own ids; its output is
-    checked against the query-tile kernel's.  Reported beside the headline."""
+def prefill_schedules(dp, bufs, fwd, steps):
+    """Both prefill schedules timed explicitly on the forward's own ids: the
+    query tiles (msa_sparse_attn_prefill_tiles) and the block-centric one
+    (msa_sparse_attn_prefill_blocks), with the one msa_sparse_attn_prefill
+    picks for this shape and the largest difference between the two outputs.
+    Reported beside the headline."""
     import torch
 
     from block_sparse_gqa_amd import device, msa
-    ids, out, lse = bufs
-    ws = device._workspace(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem, dp.q.device)
-    o2, l2 = device.alloc_out(dp)
-    device.sparse_attention_blocks(dp, ids, o2, l2, ws)   # warm-up
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    e[0].record()
-    for _ in range(steps):
-        device.sparse_attention_blocks(dp, ids, o2, l2, ws)
-    e[1].record()
-    torch.cuda.synchronize()
-    ms = e[0].elapsed_time(e[1]) / steps
-    device.sparse_attention(dp, ids, out, lse)
-    diff = float((o2.float() - out.float()).abs().max())
+    ids = bufs[0]
     flops = fwd["sparse_attn_TFLOP_per_s"] * fwd["sparse_attn_ms"] * 1e-3
-    res = {"ms": ms, "algorithmic_TFLOP": flops, "TFLOP_per_s": flops / (ms * 1e-3),
-           "frac_mfma_peak": flops / (ms * 1e-3) / MFMA_BF16_PEAK_TFLOPS, "workspace_GB": ws.numel() / 1e9,
-           "max_abs_diff_vs_query_tile": diff}
-    del ws, o2, l2
+    res, outs = {}, {}
+    for name, op, fn in (("tiles", msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, device.sparse_attention_tiles),
+                         ("blocks", msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, device.sparse_attention_blocks)):
+        ws = device._workspace(op, dp.problem, dp.q.device)
+        o, l = device.alloc_out(dp)
+        fn(dp, ids, o, l, ws)   # warm-up
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(steps):
+            fn(dp, ids, o, l, ws)
+        e[1].record()
+        torch.cuda.synchronize()
+        ms = e[0].elapsed_time(e[1]) / steps
+        res[name] = {"ms": ms, "TFLOP_per_s": flops / (ms * 1e-3),
+                     "frac_mfma_peak": flops / (ms * 1e-3) / MFMA_BF16_PEAK_TFLOPS,
+                     "workspace_GB": (ws.numel() if ws is not None else 0) / 1e9}
+        outs[name] = o
+        del ws, l
+        torch.cuda.empty_cache()
+    need = msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, dp.problem)
+    blocks_need = msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem)
+    res["auto"] = "blocks" if need == blocks_need else "tiles"
+    res["max_abs_diff"] = float((outs["tiles"].float() - outs["blocks"].float()).abs().max())
+    del outs
     torch.cuda.empty_cache()
     return res
 
@@ -273,8 +283,8 @@ def main():
     ap.add_argument("--workloads", default=",".join(WORKLOADS))
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the sparse-branch backward measurement (reported beside the headline, not in it)")
-    ap.add_argument("--no-block-centric", action="store_true",
-                    help="skip the block-centric prefill schedule measurement (reported beside the headline)")
+    ap.add_argument("--no-schedules", action="store_true",
+                    help="skip timing both prefill schedules explicitly (reported beside the headline)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement (reported beside the headline, not in it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -396,11 +406,11 @@ def main():
                 results[name]["backward"] = prefill_backward(dps[name], bufs[name], results[name],
                                                              max(args.steps // 2, 3))
 
-    if not args.no_block_centric:
+    if not args.no_schedules:
         for name in names:
             if not inputs[name].wl.is_decode:
-                results[name]["block_centric"] = prefill_block_centric(dps[name], bufs[name], results[name],
-                                                                       max(args.steps // 2, 3))
+                results[name]["schedules"] = prefill_schedules(dps[name], bufs[name], results[name],
+                                                               max(args.steps // 2, 3))
 
     if not args.no_paged:
         for name in names:

@@ -334,6 +334,26 @@ hipError_t launch_fwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
 
 size_t block_prefill_workspace_bytes(const Shape &s) { return fwd_ws(s).bytes; }
 
+// The query tiles stage the union of a tile's selections once per tile, so
+// they pay off while a staged block serves many of the tile's queries: about
+// R = Tq k / E_avg of them, with Tq queries per tile and E_avg the eligible
+// blocks of an average query of the longest sequence.  The block-centric
+// schedule does no wasted work but writes and reads back one partial output
+// per (row, slot, head).  Measured on the 32K-131K-token prefills
+// (query tiles / block-centric time): B = 64, G = 4 gave 0.40, 0.50, 0.70,
+// 1.05, 1.23 at R = 32, 16, 8, 4, 2; B = 128, G = 6 gave 0.49, 0.77, 1.14,
+// 1.65 at R = 16, 8, 4, 2 and 5.4 at about 1 (the 4-sequence 217K ragged
+// prefill).  The switch points are R = 4 (B = 64) and R = 6 (B = 128).
+bool prefill_prefers_blocks(const Shape &s) {
+    const int G = s.H / s.h;
+    if (G < 1 || G > 16 || s.max_q < 1) return false;
+    if ((long)s.total_q * s.top_k > 0x7fffffffL) return false;   // entries are row * top_k + slot
+    const double e_k = (double)((s.max_k + s.B - 1) / s.B), e_q = (double)((s.max_q + s.B - 1) / s.B);
+    const double e_avg = std::max(1.0, e_k - 0.5 * e_q);
+    const double r = (double)prefill_tile_queries(s) * std::min((double)s.top_k, e_k) / e_avg;
+    return r < (s.B >= 128 ? 6.0 : 4.0);
+}
+
 hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                       hipStream_t st) {

@@ -640,6 +640,15 @@ hipError_t launch(const Shape &s, const uint16_t *q, const uint16_t *k, const ui
 
 size_t prefill_workspace_bytes(const Shape &s) { return prefill_ws(s).bytes; }
 
+int prefill_tile_queries(const Shape &s) {
+    // One 16-row tile per wave, as many waves as keep the tile within 64
+    // queries (one mask bit per query), at most 16 (four per SIMD).
+    const int qt = 16 / (s.H / s.h);
+    const int cap = 64 / qt;
+    const int nw = cap >= 16 ? 16 : (cap >= 8 ? 8 : 4);
+    return nw * qt;
+}
+
 hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                hipStream_t st) {
@@ -662,11 +671,7 @@ hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t
                        reinterpret_cast<uint4 *>(v16), v_exp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // One 16-row tile per wave, as many waves as keep the tile within 64
-    // queries (one mask bit per query), at most 16 (four per SIMD).
-    const int qt = 16 / G;
-    const int cap = 64 / qt;
-    const int nw = cap >= 16 ? 16 : (cap >= 8 ? 8 : 4);
+    const int nw = prefill_tile_queries(s) / (16 / G);
     if (s.d == 64) {
         if (nw == 16) return launch<64, 16>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
         if (nw == 8) return launch<64, 8>(s, q, k, v16, v_exp, ids, scale, out, lse, st);

@@ -100,7 +100,13 @@ size_t msa_workspace_size(int op, const msa_problem_t *problem) {
         case MSA_OP_INDEX_TOPK:
             if (index_support(p) != MSA_SUCCESS) return (size_t)-1;
             return index_ws(p);
-        case MSA_OP_SPARSE_ATTN_PREFILL:
+        case MSA_OP_SPARSE_ATTN_PREFILL: {
+            if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
+            const Shape s = to_shape(p);
+            return msa::prefill_prefers_blocks(s) ? msa::block_prefill_workspace_bytes(s)
+                                                  : msa::prefill_workspace_bytes(s);
+        }
+        case MSA_OP_SPARSE_ATTN_PREFILL_TILES:
             if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
             return msa::prefill_workspace_bytes(to_shape(p));
         case MSA_OP_SPARSE_ATTN_DECODE:
@@ -122,10 +128,13 @@ msa_status_t msa_index_topk(const msa_problem_t *problem, const msa_bf16_t *q_id
     return msa_index_topk_ex(problem, nullptr, nullptr, q_idx, k_idx, topk_ids, workspace, workspace_bytes, stream);
 }
 
-msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
-                                     const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
-                                     msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
-                                     msa_stream_t stream) {
+namespace {
+// Which prefill schedule a call runs.
+enum class Schedule { kAuto, kTiles, kBlocks };
+
+msa_status_t prefill_call(Schedule which, const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
+                          const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out,
+                          float *lse, void *workspace, size_t workspace_bytes, msa_stream_t stream) {
     msa_status_t st = check_problem(problem);
     if (st != MSA_SUCCESS) return st;
     const msa_problem_t &p = *problem;
@@ -134,30 +143,42 @@ msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf1
         return MSA_ERROR_INVALID_VALUE;
     if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
     if ((st = attn_support(p)) != MSA_SUCCESS) return st;
-    Shape s = to_shape(p);
+    const Shape s = to_shape(p);
+    if (which == Schedule::kBlocks && (long long)p.total_q * p.top_k > 0x7fffffffLL) return MSA_ERROR_NOT_SUPPORTED;
+    const bool blocks = which == Schedule::kBlocks || (which == Schedule::kAuto && msa::prefill_prefers_blocks(s));
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (blocks) {
+        if ((st = check_ws(workspace, workspace_bytes, msa::block_prefill_workspace_bytes(s))) != MSA_SUCCESS)
+            return st;
+        return launched(msa::launch_attn_prefill_blocks(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs));
+    }
     if ((st = check_ws(workspace, workspace_bytes, msa::prefill_workspace_bytes(s))) != MSA_SUCCESS) return st;
-    return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
-                                             reinterpret_cast<hipStream_t>(stream)));
+    return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs));
+}
+}  // namespace
+
+msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
+                                     const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
+                                     msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
+                                     msa_stream_t stream) {
+    return prefill_call(Schedule::kAuto, problem, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
+                        workspace_bytes, stream);
+}
+
+msa_status_t msa_sparse_attn_prefill_tiles(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
+                                           const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
+                                           msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
+                                           msa_stream_t stream) {
+    return prefill_call(Schedule::kTiles, problem, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
+                        workspace_bytes, stream);
 }
 
 msa_status_t msa_sparse_attn_prefill_blocks(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
                                             const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale,
                                             msa_bf16_t *out, float *lse, void *workspace, size_t workspace_bytes,
                                             msa_stream_t stream) {
-    msa_status_t st = check_problem(problem);
-    if (st != MSA_SUCCESS) return st;
-    const msa_problem_t &p = *problem;
-    if (p.total_q == 0) return MSA_SUCCESS;
-    if (q == nullptr || k == nullptr || v == nullptr || topk_ids == nullptr || out == nullptr)
-        return MSA_ERROR_INVALID_VALUE;
-    if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
-    if ((st = attn_support(p)) != MSA_SUCCESS) return st;
-    if (p.num_heads / p.num_kv_heads > 16) return MSA_ERROR_NOT_SUPPORTED;
-    if ((long long)p.total_q * p.top_k > 0x7fffffffLL) return MSA_ERROR_NOT_SUPPORTED;
-    Shape s = to_shape(p);
-    if ((st = check_ws(workspace, workspace_bytes, msa::block_prefill_workspace_bytes(s))) != MSA_SUCCESS) return st;
-    return launched(msa::launch_attn_prefill_blocks(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
-                                                    reinterpret_cast<hipStream_t>(stream)));
+    return prefill_call(Schedule::kBlocks, problem, q, k, v, topk_ids, softmax_scale, out, lse, workspace,
+                        workspace_bytes, stream);
 }
 
 msa_status_t msa_sparse_attn_prefill_backward(const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,

@@ -40,9 +40,13 @@ size_t prefill_workspace_bytes(const Shape &s);
 hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                hipStream_t st);
+// Queries per workgroup tile of the query-tile kernel (G = H/h <= 16).
+int prefill_tile_queries(const Shape &s);
 // The same attention on the block-centric schedule (lists, per-block
-// partials, log-sum-exp merge).
+// partials, log-sum-exp merge), and whether it is the faster of the two for
+// a shape.
 size_t block_prefill_workspace_bytes(const Shape &s);
+bool prefill_prefers_blocks(const Shape &s);
 hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                       hipStream_t st);

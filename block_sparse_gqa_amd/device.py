@@ -81,6 +81,16 @@ def sparse_attention(dp: DeviceProblem, ids, out=None, lse=None, stream=None):
     return out, lse
 
 
+def sparse_attention_tiles(dp: DeviceProblem, ids, out=None, lse=None, ws=None, stream=None):
+    """The prefill sparse branch on the query-tile schedule (same result as sparse_attention)."""
+    if out is None:
+        out, lse = alloc_out(dp)
+    if ws is None:
+        ws = _workspace(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, dp.problem, dp.q.device)
+    msa.msa_sparse_attn_prefill_tiles(dp.problem, dp.q, dp.k, dp.v, ids, dp.wl.scale, out, lse, ws, stream)
+    return out, lse
+
+
 def sparse_attention_blocks(dp: DeviceProblem, ids, out=None, lse=None, ws=None, stream=None):
     """The prefill sparse branch on the block-centric schedule (same result as sparse_attention)."""
     if out is None:

@@ -26,6 +26,7 @@ MSA_OP_SPARSE_ATTN_PREFILL = 1
 MSA_OP_SPARSE_ATTN_DECODE = 2
 MSA_OP_SPARSE_ATTN_BACKWARD = 3
 MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS = 4
+MSA_OP_SPARSE_ATTN_PREFILL_TILES = 5
 
 SIZE_MAX = (1 << 64) - 1
 
@@ -86,6 +87,8 @@ def load():
     lib.msa_index_topk.restype = ctypes.c_int
     lib.msa_sparse_attn_prefill.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
     lib.msa_sparse_attn_prefill.restype = ctypes.c_int
+    lib.msa_sparse_attn_prefill_tiles.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
+    lib.msa_sparse_attn_prefill_tiles.restype = ctypes.c_int
     lib.msa_sparse_attn_prefill_blocks.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
     lib.msa_sparse_attn_prefill_blocks.restype = ctypes.c_int
     lib.msa_sparse_attn_decode.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
@@ -184,6 +187,13 @@ def msa_sparse_attn_prefill(problem, q, k, v, topk_ids, softmax_scale, out, lse=
     _check(load().msa_sparse_attn_prefill(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_ids),
                                           float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                           _nbytes(workspace), _stream(stream)), "msa_sparse_attn_prefill")
+
+
+def msa_sparse_attn_prefill_tiles(problem, q, k, v, topk_ids, softmax_scale, out, lse=None, workspace=None,
+                                  stream=None):
+    _check(load().msa_sparse_attn_prefill_tiles(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_ids),
+                                                float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                                _nbytes(workspace), _stream(stream)), "msa_sparse_attn_prefill_tiles")
 
 
 def msa_sparse_attn_prefill_blocks(problem, q, k, v, topk_ids, softmax_scale, out, lse=None, workspace=None,

@@ -64,7 +64,8 @@ typedef enum {
     MSA_OP_SPARSE_ATTN_PREFILL = 1,
     MSA_OP_SPARSE_ATTN_DECODE = 2,
     MSA_OP_SPARSE_ATTN_BACKWARD = 3,
-    MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS = 4
+    MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS = 4,
+    MSA_OP_SPARSE_ATTN_PREFILL_TILES = 5
 } msa_op_t;
 
 typedef struct {
@@ -124,15 +125,38 @@ msa_status_t msa_index_topk(const msa_problem_t *problem, const msa_bf16_t *q_id
  * lse      [total_q, H] float32 natural-log sum-exp of the scaled logits
  *          (written), or NULL
  * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_PREFILL) bytes,
- *          16-byte aligned: an fp16 copy of v (every value scaled by one
- *          power of two that puts max |v| in [2^14, 2^15), undone on the
- *          output) used for the P.V products, plus a few KB.
+ *          16-byte aligned; its size depends on the schedule chosen below.
+ *
+ * Two schedules compute this, and the call picks the one expected to be
+ * faster for the problem's shape (its choice depends only on the host-side
+ * fields of the problem, so msa_workspace_size gives the matching size):
+ *  - query tiles (msa_sparse_attn_prefill_tiles): a workgroup stages the
+ *    union of its queries' blocks; best while a staged block serves many of
+ *    the tile's queries (short contexts, large top_k);
+ *  - block-centric (msa_sparse_attn_prefill_blocks): best at long contexts
+ *    with a small top_k, where the tiles' unions cover nearly every block.
+ * Both give the same result to rounding.
  */
 msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf16_t *q,
                                      const msa_bf16_t *k, const msa_bf16_t *v,
                                      const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out,
                                      float *lse, void *workspace, size_t workspace_bytes,
                                      msa_stream_t stream);
+
+/*
+ * msa_sparse_attn_prefill on the query-tile schedule.  A workgroup owns up to
+ * 64 consecutive queries of one group (all G heads), forms the union of the
+ * blocks they selected and streams each union block through LDS once.
+ * Arguments, layouts and errors as for msa_sparse_attn_prefill.
+ * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_PREFILL_TILES)
+ * bytes, 16-byte aligned: an fp16 copy of v (every value scaled by one power
+ * of two that puts max |v| in [2^14, 2^15), undone on the output) used for
+ * the P.V products, plus a few KB.
+ */
+msa_status_t msa_sparse_attn_prefill_tiles(const msa_problem_t *problem, const msa_bf16_t *q,
+                                           const msa_bf16_t *k, const msa_bf16_t *v, const int32_t *topk_ids,
+                                           float softmax_scale, msa_bf16_t *out, float *lse, void *workspace,
+                                           size_t workspace_bytes, msa_stream_t stream);
 
 /*
  * Sparse branch, decode (max_seqlen_q == 1, total_q == num_seqs): the same

@@ -63,8 +63,21 @@ def test_workspace_size(lib):
     assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p)) == 128 * 2 * 4 * 4
     # fp16 copy of V [total_k, h, d] (256-byte aligned) + 1024 partial maxima + the scale exponent
     vbytes = p.total_k * p.num_kv_heads * p.head_dim * 2
-    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == \
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p)) == \
         (vbytes + 255) // 256 * 256 + 1024 * 4 + 256
+    # short context, every block selected: the prefill call runs the query tiles
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == \
+        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
+    # 131072-token prefill with k = 16 and B = 128: the block-centric schedule
+    long_ctx = prob(total_q=131072, total_k=131072, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,
+                    num_kv_heads=8, block_size=128, top_k=16)
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(long_ctx)) == \
+        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(long_ctx))
+    # the 32768-token, k = 32, B = 64 prefill stays on the query tiles
+    p32k = prob(total_q=32768, total_k=32768, max_seqlen_q=32768, max_seqlen_k=32768, num_heads=32, num_kv_heads=8,
+                top_k=32)
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k)) == \
+        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p32k))
     # decode needs max_seqlen_q == 1
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_DECODE, ctypes.byref(p)) == msa.SIZE_MAX
     d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)

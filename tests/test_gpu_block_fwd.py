@@ -38,7 +38,7 @@ def run(inp):
     dp = device.upload(inp)
     ids = device.index_topk(dp)
     out_b, lse_b = device.sparse_attention_blocks(dp, ids)
-    out_q, lse_q = device.sparse_attention(dp, ids)
+    out_q, lse_q = device.sparse_attention_tiles(dp, ids)
     torch.cuda.synchronize()
     res = dict(ids=ids.cpu().numpy(), out_b=out_b.float().cpu().numpy(), lse_b=lse_b.cpu().numpy(),
                out_q=out_q.float().cpu().numpy(), lse_q=lse_q.cpu().numpy())

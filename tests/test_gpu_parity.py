@@ -43,6 +43,14 @@ def run_gpu(inp, ids_override=None):
         out2, lse2 = device.sparse_attention(dp, ids2)
         res["out_given"] = out2.float().cpu().numpy()
         res["lse_given"] = lse2.cpu().numpy()
+        if not inp.wl.is_decode:
+            # both prefill schedules explicitly, whichever the call above chose
+            for name, fn in (("tiles", device.sparse_attention_tiles), ("blocks", device.sparse_attention_blocks)):
+                o3, l3 = fn(dp, ids2)
+                res[f"out_{name}"] = o3.float().cpu().numpy()
+                res[f"lse_{name}"] = l3.cpu().numpy()
+                del o3, l3
+                torch.cuda.empty_cache()
     torch.cuda.synchronize()
     del dp
     return res
@@ -66,6 +74,10 @@ def check_case(inp, rows=None, label=""):
     ref_out, ref_lse = oracle.sparse_attention(inp, ref_ids, rows)
     e1 = parity.assert_close(g["out_given"][rows], ref_out, f"{label} attention (oracle ids)")
     e2 = parity.assert_close(g["lse_given"][rows], ref_lse, f"{label} lse (oracle ids)")
+    for name in ("tiles", "blocks"):
+        if f"out_{name}" in g:
+            parity.assert_close(g[f"out_{name}"][rows], ref_out, f"{label} attention, {name} schedule (oracle ids)")
+            parity.assert_close(g[f"lse_{name}"][rows], ref_lse, f"{label} lse, {name} schedule (oracle ids)")
     same = np.array([np.array_equal(g["ids"][r], ref_ids[i]) for i, r in enumerate(rows)])
     e3 = parity.assert_close(g["out"][rows[same]], ref_out[same], f"{label} end-to-end attention")
     say(f"[{label}] attention max err: oracle-ids {e1:.3g}, lse {e2:.3g}, end-to-end {e3:.3g} "
