@@ -117,6 +117,11 @@ __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict_
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
         mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
     }
+    // Equal in every lane after the butterfly; reading them into scalar
+    // registers makes the search below scalar-controlled (no exec-mask
+    // bookkeeping per step, the candidate is a scalar operand of the compares).
+    mx = __builtin_amdgcn_readfirstlane(mx);
+    mn = __builtin_amdgcn_readfirstlane(mn);
     // T = largest value with count(key >= T) >= k (the k-th largest key).  All
     // valid keys share the bits above `top`; start there with zeros below.
     const int top = (mx == mn) ? -1 : 31 - __builtin_clz(mx ^ mn);
