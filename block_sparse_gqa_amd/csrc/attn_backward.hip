@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256, 2) void bwd_block(
     const int q_begin = cu_q[s], shift = len_k - (cu_q[s + 1] - q_begin);
     const int G = H / h;
     const int qpc = kRows / G;                   // queries per chunk
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loops over tiles
     const int l16 = lane & 15, q4 = lane >> 4;
     const int t_valid = min(B, len_k - j * B);   // tokens of the block inside the sequence
 

@@ -89,7 +89,8 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
     const int k_begin = cu_k[s], len_k = cu_k[s + 1] - k_begin;
     const int q_begin = cu_q[s], shift = len_k - (cu_q[s + 1] - q_begin);
     const int G = H / h, qpt = 16 / G, rows_used = qpt * G;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop over the tiles
     const int l16 = lane & 15, q4 = lane >> 4;
     const int t_valid = min(B, len_k - j * B);   // tokens of the block inside the sequence
 

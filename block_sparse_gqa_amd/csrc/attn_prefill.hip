@@ -246,7 +246,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const int e_tile = p_last / B + 1;
     const int nsub = B / 64;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar control flow below
     const int l16 = lane & 15, q4 = lane >> 4;
 
     // This lane's row (query qi of the wave's tile, head `head` of the group).
@@ -465,8 +466,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
 
         // Items are the 64-token sub-blocks of the listed blocks; a trailing
         // sub-block that starts after the tile's last query is dropped.
+        count = __builtin_amdgcn_readfirstlane(count);   // the same in every lane
         int nitems = count * nsub;
         if (nsub > 1 && count > 0 && (int)lds_u32(list_u0 + 4 * (count - 1)) * B + 64 > p_last) --nitems;
+        nitems = __builtin_amdgcn_readfirstlane(nitems);
         auto t0_of = [&](int it) {
             return (int)lds_u32(list_u0 + 4 * (it / nsub)) * B + (it % nsub) * 64;
         };

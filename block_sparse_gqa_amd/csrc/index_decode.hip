@@ -49,7 +49,8 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     const int k_begin = cu_k[s], len_k = cu_k[s + 1] - k_begin;
     const int p = len_k - 1;
     const int E = p / B + 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar block loop
     // Blocks are dealt out round-robin over every wave of the sequence, so the
     // waves in flight at any moment read neighbouring blocks.
     const int nwaves = gridDim.x * kWaves;
