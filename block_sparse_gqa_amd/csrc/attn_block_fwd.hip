@@ -27,8 +27,8 @@
 // the Q rows two tiles ahead in registers.
 //
 // Pass 3 (fwd_merge): per (row, head), the partials of the row's valid slots
-// merge by log-sum-exp into O (bf16) and LSE (natural log), summed in slot
-// order.
+// merge by log-sum-exp into O (bf16) and LSE (natural log) in one pass, in a
+// fixed order; one wave takes the G heads of a (row, group).
 #include <algorithm>
 
 #include "msa_device.h"
@@ -232,64 +232,76 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
     }
 }
 
-// O[row, head] and LSE from the partials of the row's valid slots.  One wave
-// per (row, head); lane = (slot lane group, 16-byte chunk of a partial row),
-// so every load instruction reads whole partial rows.
+// O[row, head] and LSE from the partials of the row's valid slots, in one
+// pass.  One wave per (row, group), taking the group's G heads in turn (the
+// row's sequence lookup and ids are shared by them); lane = (slot lane group,
+// 16-byte chunk of a partial row), so every load instruction reads whole
+// partial rows.  Each lane merges its slots online (running max of their
+// log2-sum-exp, the sums rescaled when it grows), then the lanes' results are
+// brought to the wave's max and summed.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ part_o, const float2 *__restrict__ part_w,
                                                  const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
-                                                 const int32_t *__restrict__ cu_k, int num_seqs, long n_rows, int H,
+                                                 const int32_t *__restrict__ cu_k, int num_seqs, long n_pairs, int H,
                                                  int h, int B, int top_k, uint16_t *__restrict__ out,
                                                  float *__restrict__ lse) {
     constexpr int CPR = D / 8;       // 16-byte chunks per partial row
     constexpr int NSO = 64 / CPR;    // slot lane groups
-    const long rh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (rh >= n_rows) return;
+    const long rg = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rg >= n_pairs) return;
     const int lane = threadIdx.x & 63, c = lane % CPR, so = lane / CPR;
-    const int row = (int)(rh / H), head = (int)(rh % H), g = head / (H / h);
+    const int row = (int)(rg / h), g = (int)(rg % h), G = H / h;
     const int s = seq_of_row(cu_q, num_seqs, row);
     const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
     const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
     const size_t base = (size_t)row * top_k;
 
-    float m = -INFINITY;
-    for (int a = lane; a < top_k; a += 64) {
-        const int j = sel[a];
-        if (j >= 0 && j <= p / B) m = fmaxf(m, part_w[(base + a) * H + head].x);
-    }
+    for (int hh = 0; hh < G; ++hh) {
+        const int head = g * G + hh;
+        const size_t rh = (size_t)row * H + head;
+        float m = -INFINITY, acc[8], den = 0.f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float mu = m == -INFINITY ? 0.f : m;
-
-    float acc[8], den = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll 4
-    for (int a = so; a < top_k; a += NSO) {
-        const int j = sel[a];
-        const bool ok = j >= 0 && j <= p / B;
-        const size_t sh = (base + (ok ? a : 0)) * H + head;
-        const float2 w = part_w[sh];
-        const uint4 x = load16(part_o + sh * D + 8 * c);
-        const float wn = ok ? fast_exp2(w.x - mu + w.y) : 0.f;   // weight of the stored (scaled) partial
-        const float wd = ok ? fast_exp2(w.x - mu) : 0.f;
-        const f16x8 hv = as_f16x8(x);
+        for (int a = so; a < top_k; a += NSO) {
+            const int j = sel[a];
+            const bool ok = j >= 0 && j <= p / B;
+            const size_t sh = (base + (ok ? a : 0)) * H + head;
+            const float2 w = part_w[sh];
+            const uint4 x = load16(part_o + sh * D + 8 * c);
+            if (ok) {   // skipped slots hold no partial
+                const float m_new = fmaxf(m, w.x);
+                const float alpha = fast_exp2(m - m_new);   // 0 while m is -inf
+                const float wd = fast_exp2(w.x - m_new);
+                const float wn = wd * __builtin_ldexpf(1.0f, (int)w.y);   // the stored partial is scaled by 2^-e
+                const f16x8 hv = as_f16x8(x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += ok ? wn * (float)hv[i] : 0.f;   // skipped slots hold no partial
-        den += c == 0 ? wd : 0.f;
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(wn, (float)hv[i], acc[i] * alpha);
+                den = fmaf(den, alpha, wd);
+                m = m_new;
+            }
+        }
+        // bring every lane to the wave's max, then sum the slot lane groups
+        float mw = m;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o, 64));
+        const float scale = m == -INFINITY ? 0.f : fast_exp2(m - mw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= scale;
+        den = c == 0 ? den * scale : 0.f;   // one copy of each slot's weight per slot lane group
+#pragma unroll
+        for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o, 64);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o, 64);
+        const float inv = den > 0.f ? 1.0f / den : 0.f;
+        if (so == 0)
+            *reinterpret_cast<uint4 *>(out + rh * D + 8 * c) =
+                uint4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+        if (lse != nullptr && lane == 0) lse[rh] = den > 0.f ? (mw + __log2f(den)) * 0.69314718055994531f : -INFINITY;
     }
-#pragma unroll
-    for (int o = CPR; o < 64; o <<= 1)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o, 64);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o, 64);
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
-    if (so == 0)
-        *reinterpret_cast<uint4 *>(out + (size_t)rh * D + 8 * c) =
-            uint4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                  pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-    if (lse != nullptr && lane == 0) lse[rh] = den > 0.f ? (mu + __log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
 struct FwdWs {
@@ -325,9 +337,9 @@ hipError_t launch_fwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
     hipLaunchKernelGGL((fwd_block<D, B>), dim3((unsigned)w.lists.nb_max, s.h), dim3(64 * fwd_waves<B>()), 0, st, q, k, v, s.cu_q,
                        s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max, s.top_k,
                        scale * kLog2e, part_o, part_w);
-    const long rows = (long)s.total_q * s.H;
-    hipLaunchKernelGGL((fwd_merge<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, part_o, part_w, ids, s.cu_q,
-                       s.cu_k, s.num_seqs, rows, s.H, s.h, s.B, s.top_k, out, lse);
+    const long pairs = (long)s.total_q * s.h;
+    hipLaunchKernelGGL((fwd_merge<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, part_o, part_w, ids, s.cu_q,
+                       s.cu_k, s.num_seqs, pairs, s.H, s.h, s.B, s.top_k, out, lse);
     return hipGetLastError();
 }
 
