@@ -13,9 +13,10 @@
 // Pass 2 (fwd_block): one workgroup per (group, block).  The block's K (bf16)
 // and V (fp16, scaled by a power of two 2^-e chosen from the block's largest
 // |v| so that every value and every partial output fits fp16) sit in LDS.
-// Each wave takes 16-row tiles of the list (16/G selecting queries x G
-// heads), gathers their Q rows straight into the MFMA B operand (two tiles
-// ahead) and computes
+// Each wave takes 32-row tiles of the list (32/G selecting queries x G
+// heads, two 16-row MFMA tiles sharing every K and V operand read), gathers
+// their Q rows straight into the MFMA B operands (one tile ahead) and
+// computes
 //     S^T = K . Q^T         v_mfma_f32_16x16x32_bf16, A = K rows from LDS;
 //     P   = 2^(S c2 - m)    m = the row's max over the block's visible tokens;
 //     O^T = V^T . P^T       v_mfma_f32_16x16x32_f16, A = V^T (transposing LDS
@@ -23,8 +24,8 @@
 // Every (row, slot, head) gets a partial: O / l as fp16 (times 2^-e) and the
 // pair (m + log2 l, e), the partial rows staged through a per-wave LDS tile
 // so that stores cover whole rows.  No workgroup barrier after the staging:
-// each wave walks its own tiles, with the list entries three tiles ahead and
-// the Q rows two tiles ahead in registers.
+// each wave walks its own tiles, with the list entries two tiles ahead and
+// the Q rows one tile ahead in registers.
 //
 // Pass 3 (fwd_merge): per (row, head), the partials of the row's valid slots
 // merge by log-sum-exp into O (bf16) and LSE (natural log) in one pass, in a
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
     if (nq == 0) return;
     const int k_begin = cu_k[s], len_k = cu_k[s + 1] - k_begin;
     const int q_begin = cu_q[s], shift = len_k - (cu_q[s + 1] - q_begin);
-    const int G = H / h, qpt = 16 / G, rows_used = qpt * G;
+    const int G = H / h;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop over the tiles
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -131,103 +132,142 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
     }
     __syncthreads();
 
-    // This lane's row of a tile: query l16 / G of the tile, head g*G + l16 % G.
-    const int qi = l16 / G, hd = l16 % G;
+    // Tiles of 32 rows (32/G selecting queries x G heads) as two 16-row MFMA
+    // tiles mt = 0, 1 that share every K and V operand read.  This lane's row
+    // in tile mt is r = 16 mt + l16: query r / G of the tile, head g*G + r % G.
+    constexpr int MT = 2;
+    const int qpt = (16 * MT) / G, rows_used = qpt * G;
+    int qi[MT], hd[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        qi[mt] = (16 * mt + l16) / G;
+        hd[mt] = (16 * mt + l16) % G;
+    }
     const int ntiles = (nq + qpt - 1) / qpt;
-    auto entry = [&](int t) {   // row * top_k + slot, or -1
-        const int x = t * qpt + qi;
-        return (t < ntiles && l16 < rows_used && x < nq) ? entries[e0 + x] : -1;
+    auto entry = [&](int t, int mt) {   // row * top_k + slot, or -1
+        const int x = t * qpt + qi[mt];
+        return (t < ntiles && 16 * mt + l16 < rows_used && x < nq) ? entries[e0 + x] : -1;
     };
-    auto load_q = [&](uint4 (&qo)[KS], int ent) {   // row 0 stands in for unused lanes
-        const size_t base = ((size_t)(ent >= 0 ? ent / top_k : 0) * H + g * G + hd) * D + 8 * q4;
+    auto load_q = [&](uint4 (&qo)[KS], int ent, int hh) {   // row 0 stands in for unused lanes
+        const size_t base = ((size_t)(ent >= 0 ? ent / top_k : 0) * H + g * G + hh) * D + 8 * q4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qo[ks] = load16(q + base + 32 * ks);
     };
 
     int t = wave;
-    int ent_cur = entry(t), ent_next = entry(t + NW), ent_n2 = entry(t + 2 * NW);
-    uint4 qc[KS], qn[KS] = {}, qn2[KS] = {};
-    load_q(qc, ent_cur);
-    if (t + NW < ntiles) load_q(qn, ent_next);
+    int ent_cur[MT], ent_next[MT];
+    uint4 qc[MT][KS], qn[MT][KS] = {};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        ent_cur[mt] = entry(t, mt);
+        ent_next[mt] = entry(t + NW, mt);
+        load_q(qc[mt], ent_cur[mt], hd[mt]);
+    }
     for (; t < ntiles; t += NW) {
-        const int ent_after = entry(t + 3 * NW);
-        if (t + 2 * NW < ntiles) load_q(qn2, ent_n2);
+        int ent_after[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) ent_after[mt] = entry(t + 2 * NW, mt);
+        if (t + NW < ntiles) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) load_q(qn[mt], ent_next[mt], hd[mt]);
+        }
 
-        f32x4 sa[TT];
+        f32x4 sa[MT][TT];
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-            sa[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sa[tt] = mfma16x16x32(as_bf16x8(lds_row8(kt, 16 * tt + l16, 4 * ks + q4)), as_bf16x8(qc[ks]), sa[tt]);
+            for (int mt = 0; mt < MT; ++mt) sa[mt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = as_bf16x8(lds_row8(kt, 16 * tt + l16, 4 * ks + q4));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) sa[mt][tt] = mfma16x16x32(a, as_bf16x8(qc[mt][ks]), sa[mt][tt]);
+            }
         }
-        // Visible tokens of this lane's row: block token index <= lim.
-        const int row = ent_cur >= 0 ? ent_cur / top_k : -1;
-        const int lim = row >= 0 ? shift + (row - q_begin) - j * B : -1;
-        float mx = -INFINITY;
+        // Visible tokens of this lane's rows: block token index <= lim.
+        float mu[MT], lsum[MT];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = ent_cur[mt] >= 0 ? ent_cur[mt] / top_k : -1;
+            const int lim = row >= 0 ? shift + (row - q_begin) - j * B : -1;
+            float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = 16 * tt + 4 * q4 + i <= lim ? sa[tt][i] * c2 : -INFINITY;
-                sa[tt][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = max_xor32(max_xor16(mx));
-        const float mu = mx == -INFINITY ? 0.f : mx;
-        float lsum = 0.f;
+            for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+                for (int i = 0; i < 4; ++i) {
+                    const float x = 16 * tt + 4 * q4 + i <= lim ? sa[mt][tt][i] * c2 : -INFINITY;
+                    sa[mt][tt][i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = max_xor32(max_xor16(mx));
+            mu[mt] = mx == -INFINITY ? 0.f : mx;
+            float ls = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(sa[tt][i] - mu);
-                sa[tt][i] = p;
-                lsum += p;
-            }
-        lsum = sum_xor32(sum_xor16(lsum));
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = fast_exp2(sa[mt][tt][i] - mu[mt]);
+                    sa[mt][tt][i] = pv;
+                    ls += pv;
+                }
+            lsum[mt] = sum_xor32(sum_xor16(ls));
+        }
 
-        f32x4 oa[DT];
+        f32x4 oa[MT][DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oa[mt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s32 = 0; s32 < B / 32; ++s32) {
             // B = P^T: k slot 8*q4 + i <- token 32*s32 + 4*q4 + i, slot 8*q4 + 4 + i <- token 32*s32 + 16 + 4*q4 + i
-            const f16x8 pb = as_f16x8(uint4{pack_f16x2(sa[2 * s32][0], sa[2 * s32][1]),
-                                            pack_f16x2(sa[2 * s32][2], sa[2 * s32][3]),
-                                            pack_f16x2(sa[2 * s32 + 1][0], sa[2 * s32 + 1][1]),
-                                            pack_f16x2(sa[2 * s32 + 1][2], sa[2 * s32 + 1][3])});
+            f16x8 pb[MT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                oa[dt] = mfma16x16x32_f16(as_f16x8(lds_tr_rows(vt, 32 * s32, dt)), pb, oa[dt]);
+            for (int mt = 0; mt < MT; ++mt)
+                pb[mt] = as_f16x8(uint4{pack_f16x2(sa[mt][2 * s32][0], sa[mt][2 * s32][1]),
+                                        pack_f16x2(sa[mt][2 * s32][2], sa[mt][2 * s32][3]),
+                                        pack_f16x2(sa[mt][2 * s32 + 1][0], sa[mt][2 * s32 + 1][1]),
+                                        pack_f16x2(sa[mt][2 * s32 + 1][2], sa[mt][2 * s32 + 1][3])});
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f16x8 va = as_f16x8(lds_tr_rows(vt, 32 * s32, dt));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) oa[mt][dt] = mfma16x16x32_f16(va, pb[mt], oa[mt][dt]);
+            }
         }
-        // O / l (fp16) goes through this wave's LDS tile so that every store
-        // instruction writes whole partial rows (16 lanes x 16 bytes per row
-        // for d = 128).
-        const float inv = row >= 0 ? 1.0f / lsum : 0.f;
+        // O / l (fp16) goes through this wave's LDS tile, 16 rows at a time,
+        // so that every store instruction writes whole partial rows (16 lanes x
+        // 16 bytes per row for d = 128).
         char *my = ot[wave];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<uint2 *>(my + l16 * OSTR + (16 * dt + 4 * q4) * 2) =
-                uint2{pack_f16x2(oa[dt][0] * inv, oa[dt][1] * inv), pack_f16x2(oa[dt][2] * inv, oa[dt][3] * inv)};
-        wave_lds_sync();
         constexpr int CPR = D / 8;      // 16-byte chunks per row
         constexpr int RPI = 64 / CPR;   // rows per store instruction
 #pragma unroll
-        for (int x = 0; x < 16 / RPI; ++x) {
-            const int r = x * RPI + lane / CPR, c = lane % CPR;
-            const int er = __shfl(ent_cur, r, 64);   // the entry of tile row r (held by lane r)
-            const uint4 val = *reinterpret_cast<const uint4 *>(my + r * OSTR + 16 * c);
-            if (er >= 0) *reinterpret_cast<uint4 *>(part_o + ((size_t)er * H + g * G + r % G) * D + 8 * c) = val;
-        }
-        if (row >= 0 && q4 == 0)
-            part_w[(size_t)ent_cur * H + g * G + hd] = make_float2(mu + __log2f(lsum), (float)e);
-        ent_cur = ent_next;
-        ent_next = ent_n2;
-        ent_n2 = ent_after;
+        for (int mt = 0; mt < MT; ++mt) {
+            const float inv = ent_cur[mt] >= 0 ? 1.0f / lsum[mt] : 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qc[ks] = qn[ks];
-            qn[ks] = qn2[ks];
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<uint2 *>(my + l16 * OSTR + (16 * dt + 4 * q4) * 2) =
+                    uint2{pack_f16x2(oa[mt][dt][0] * inv, oa[mt][dt][1] * inv),
+                          pack_f16x2(oa[mt][dt][2] * inv, oa[mt][dt][3] * inv)};
+            wave_lds_sync();
+#pragma unroll
+            for (int x = 0; x < 16 / RPI; ++x) {
+                const int r = x * RPI + lane / CPR, c = lane % CPR;
+                const int er = __shfl(ent_cur[mt], r, 64);   // the entry of tile row 16 mt + r (held by lane r)
+                const uint4 val = *reinterpret_cast<const uint4 *>(my + r * OSTR + 16 * c);
+                if (er >= 0)
+                    *reinterpret_cast<uint4 *>(part_o + ((size_t)er * H + g * G + (16 * mt + r) % G) * D + 8 * c) = val;
+            }
+            wave_lds_sync();   // the tile's reads are done before the next rows are written
+            if (ent_cur[mt] >= 0 && q4 == 0)
+                part_w[(size_t)ent_cur[mt] * H + g * G + hd[mt]] = make_float2(mu[mt] + __log2f(lsum[mt]), (float)e);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            ent_cur[mt] = ent_next[mt];
+            ent_next[mt] = ent_after[mt];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qc[mt][ks] = qn[mt][ks];
         }
     }
 }
