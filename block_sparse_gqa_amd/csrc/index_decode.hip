@@ -63,6 +63,14 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     for (int ks = 0; ks < KS; ++ks)
         qop[ks] = as_bf16x8(load16_if(q_idx + ((size_t)row * h + g) * DI + 32 * ks + 8 * q4, g < h, q_idx));
 
+    // Paged cache: lane i holds the page of the wave's i-th block, read once
+    // up front so that no block's loads wait on a table read.
+    int pages = 0;
+    if constexpr (PAGED) {
+        const long ji = (long)j_first + (long)lane * nwaves;
+        if (ji < E) pages = min(max(table[(size_t)s * table_stride + ji], 0), num_pages - 1);
+    }
+
     // Plain loads (no select on the loaded values, so nothing waits for them
     // until the block is used); rows past the sequence end repeat its last
     // key and are masked below.
@@ -72,7 +80,9 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
         // pool row of the block's first token
         size_t row0 = (size_t)(k_begin + t0);
         if constexpr (PAGED) {
-            const int pg = min(max(table[(size_t)s * table_stride + j], 0), num_pages - 1);
+            const int i = (j - j_first) / nwaves;   // the wave's i-th block
+            const int pg = i < 64 ? __builtin_amdgcn_readlane(pages, i)
+                                  : min(max(table[(size_t)s * table_stride + j], 0), num_pages - 1);
             row0 = (size_t)pg * B;
         }
 #pragma unroll
