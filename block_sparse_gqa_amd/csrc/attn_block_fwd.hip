@@ -41,22 +41,6 @@ namespace {
 
 constexpr int kStride = 288;   // LDS row stride of K and V in bytes (32 mod 256: conflict free)
 
-// Row r of a row-major 16-bit tile, 8 values at column 8 * c8.
-__device__ __forceinline__ uint4 lds_row8(const char *tile, int r, int c8) {
-    return *reinterpret_cast<const uint4 *>(tile + r * kStride + 16 * c8);
-}
-
-// Transposing reads of rows r0 + 4*q4 .. +3 and r0 + 16 + 4*q4 .. +3 of a
-// row-major 16-bit tile, column 16*ct + (lane % 16): an MFMA operand whose k
-// slots 8*q4 + i are those rows.
-__device__ __forceinline__ uint4 lds_tr_rows(const char *tile, int r0, int ct) {
-    const int lane = lane_id(), l16 = lane & 15, q4 = lane >> 4;
-    const char *p = tile + (r0 + 4 * q4 + (l16 >> 2)) * kStride + 8 * (l16 & 3) + 32 * ct;
-    const uint2 x = __builtin_bit_cast(uint2, lds_read_tr16(p));
-    const uint2 y = __builtin_bit_cast(uint2, lds_read_tr16(p + 16 * kStride));
-    return uint4{x.x, x.y, y.x, y.y};
-}
-
 // Waves per workgroup: B = 128 keeps two waves per SIMD with one workgroup
 // per CU (its K/V tiles take 72 KB of LDS).
 template <int B>
@@ -179,7 +163,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
             for (int mt = 0; mt < MT; ++mt) sa[mt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = as_bf16x8(lds_row8(kt, 16 * tt + l16, 4 * ks + q4));
+                const bf16x8 a = as_bf16x8(lds_row8<kStride>(kt, 16 * tt + l16, 4 * ks + q4));
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) sa[mt][tt] = mfma16x16x32(a, as_bf16x8(qc[mt][ks]), sa[mt][tt]);
             }
@@ -230,7 +214,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
                                         pack_f16x2(sa[mt][2 * s32 + 1][2], sa[mt][2 * s32 + 1][3])});
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const f16x8 va = as_f16x8(lds_tr_rows(vt, 32 * s32, dt));
+                const f16x8 va = as_f16x8(lds_tr_rows<kStride>(vt, 32 * s32, dt));
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) oa[mt][dt] = mfma16x16x32_f16(va, pb[mt], oa[mt][dt]);
             }

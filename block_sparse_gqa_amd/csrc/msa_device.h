@@ -114,6 +114,26 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void *lds_ptr) {
         (lds_i16x4 *)((__attribute__((address_space(3))) char *)lds_ptr));
 }
 
+// 16-byte read of row r of a row-major 16-bit LDS tile (row stride STRIDE
+// bytes), 8 values from column 8 * c8: the A/B operand of lane (r, c8).
+template <int STRIDE>
+__device__ __forceinline__ uint4 lds_row8(const char *tile, int r, int c8) {
+    return *reinterpret_cast<const uint4 *>(tile + r * STRIDE + 16 * c8);
+}
+
+// Transposing reads of rows r0 + 4*q4 .. +3 and r0 + 16 + 4*q4 .. +3 of a
+// row-major 16-bit LDS tile (row stride STRIDE bytes), column
+// 16*ct + (lane % 16): the 8 values of an MFMA operand whose k slots
+// 8*q4 + i are those rows.
+template <int STRIDE>
+__device__ __forceinline__ uint4 lds_tr_rows(const char *tile, int r0, int ct) {
+    const int lane = (int)__lane_id(), l16 = lane & 15, q4 = lane >> 4;
+    const char *p = tile + (r0 + 4 * q4 + (l16 >> 2)) * STRIDE + 8 * (l16 & 3) + 32 * ct;
+    const uint2 x = __builtin_bit_cast(uint2, lds_read_tr16(p));
+    const uint2 y = __builtin_bit_cast(uint2, lds_read_tr16(p + 16 * STRIDE));
+    return uint4{x.x, x.y, y.x, y.y};
+}
+
 // Order-preserving map of a float32 onto uint32 (larger float -> larger key).
 // -0.0 is folded onto +0.0 so both zeros tie.
 __device__ __forceinline__ uint32_t order_key(float f) {
