@@ -74,7 +74,7 @@ __device__ __forceinline__ bf16x8 row8(const char *tile, int r, int c8) {
 }
 
 template <int D, int B>
-__global__ __launch_bounds__(256, 2) void bwd_block(
+__global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
