@@ -56,6 +56,8 @@ CASES = [
     # 16 groups x 1094 key blocks = 17504 (group, block) keys: more than the
     # LDS histogram of the counting pass holds, so the global-atomic count runs
     ("bwd_many_keys", (64, 64), (40000, 30000), 16, 16, 64, 32, 64, 3),
+    # empty sequences inside the batch (no rows, no key blocks)
+    ("bwd_empty_seqs", (0, 300, 0, 129), (0, 300, 0, 129), 8, 2, 128, 64, 64, 3),
 ]
 
 

@@ -5,7 +5,7 @@ same seeded inputs.
 * attention: atol 2e-3 / rtol 1e-2, run with the oracle's ids (so selection and
   attention are pinned separately), and end to end with the GPU's own ids on
   every row where those equal the oracle's;
-* edge cases: ragged packing, partial final blocks, rows with fewer eligible
+* edge cases: ragged packing, empty sequences inside a batch, partial final blocks, rows with fewer eligible
   blocks than k, k covering every block, G = 1 and G = 16, decode contexts
   shorter than one block, planted and all-tie closed forms, determinism.
 The five named workloads run at full size with the launch configuration the
@@ -98,6 +98,7 @@ SMALL = [
     ("decode_B128_d64", (1, 1, 1), (5000, 129, 128), 16, 16, 64, 32, 128, 5, False),
     ("decode_k_over_E", (1, 1), (200, 3000), 16, 4, 128, 64, 64, 64, False),
     ("chunked_prefill", (100, 37), (300, 400), 8, 4, 128, 64, 64, 3, False),
+    ("empty_sequences", (0, 300, 0, 129), (0, 300, 0, 129), 8, 2, 128, 64, 64, 3, True),
 ]
 
 
