@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
                 const int er = __shfl(ent_cur[mt], r, 64);   // the entry of tile row 16 mt + r (held by lane r)
                 const uint4 val = *reinterpret_cast<const uint4 *>(my + r * OSTR + 16 * c);
                 if (er >= 0)
-                    *reinterpret_cast<uint4 *>(part_o + ((size_t)er * H + g * G + (16 * mt + r) % G) * D + 8 * c) = val;
+                    store16_nt(part_o + ((size_t)er * H + g * G + (16 * mt + r) % G) * D + 8 * c, val);
             }
             wave_lds_sync();   // the tile's reads are done before the next rows are written
             if (ent_cur[mt] >= 0 && q4 == 0)
@@ -388,7 +388,7 @@ bool prefill_prefers_blocks(const Shape &s) {
     const double e_k = (double)((s.max_k + s.B - 1) / s.B), e_q = (double)((s.max_q + s.B - 1) / s.B);
     const double e_avg = std::max(1.0, e_k - 0.5 * e_q);
     const double r = (double)prefill_tile_queries(s) * std::min((double)s.top_k, e_k) / e_avg;
-    return r < (s.B >= 128 ? 6.0 : 4.0);
+    return r < (s.B >= 128 ? 9.0 : 5.0);
 }
 
 hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,

@@ -54,6 +54,14 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte global store marked non-temporal (the nt bit): for write-once data
+// that a later kernel reads, so that it streams to memory instead of taking
+// cache lines that the running kernel's own re-read operands hold.
+__device__ __forceinline__ void store16_nt(void *p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
+
 // 16-byte global load that yields zeros when `ok` is false.  The load itself
 // is unconditional (one global_load_dwordx4): when `ok` is false it reads the
 // always-valid address `safe` instead of `p`, and the value is then dropped.

@@ -78,6 +78,11 @@ def test_workspace_size(lib):
                 top_k=32)
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k)) == \
         lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p32k))
+    # the same with k = 16: a staged block serves about 4 queries of a tile, so the block-centric schedule runs
+    p32k16 = prob(total_q=32768, total_k=32768, max_seqlen_q=32768, max_seqlen_k=32768, num_heads=32, num_kv_heads=8,
+                  top_k=16)
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k16)) == \
+        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(p32k16))
     # decode needs max_seqlen_q == 1
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_DECODE, ctypes.byref(p)) == msa.SIZE_MAX
     d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)
