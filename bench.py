@@ -108,13 +108,14 @@ def cpu_baseline(inputs, budget_s=24.0, seed=7):
             "sample": "; ".join(parts) + "; each part extrapolated linearly to its full workload"}
 
 
-def measured_traffic(kernel_file, symbol, launches_per_call):
+def measured_traffic(kernel_file, symbol, launches_per_call, workload):
     """HBM bytes per call of the dominant kernel from the committed PMC summary.
 
     The summary records FETCH_SIZE / WRITE_SIZE per dispatch, the scale factors
-    a plain copy of known size gives for the same counters, and the SHA-256 of
-    the kernel source the counters were taken on.  If that source has changed
-    since, the counters no longer describe the kernel and None is returned.
+    a plain copy of known size gives for the same counters, the SHA-256 of the
+    kernel source the counters were taken on, and the workloads they were
+    taken on.  If that source has changed since, or the workload is another,
+    the counters do not describe this launch and None is returned.
     """
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -125,6 +126,8 @@ def measured_traffic(kernel_file, symbol, launches_per_call):
         with open(src, "rb") as f:
             digest = hashlib.sha256(f.read()).hexdigest()
     except OSError:
+        return None
+    if workload not in table.get("workload", "").replace("+", " ").split():
         return None
     for e in table.get("kernels", []):
         if e.get("symbol") == symbol and e.get("source_sha256") == digest:
@@ -380,9 +383,13 @@ def main():
                       "TFLOP_per_s": tot, "frac_mfma_peak": tot / MFMA_BF16_PEAK_TFLOPS,
                       "index_topk_TFLOP_per_s": tf_i, "sparse_attn_TFLOP_per_s": tf_a})
             kernels.append(("msa_index_topk[%s]" % name, t_idx, "mfma", alg["index_flops"], None))
-            # one launch of attn_prefill_tile per call
+            # One launch of attn_prefill_tile per call on the query-tile schedule.  The committed
+            # counters cover that kernel on the workloads they name; the block-centric schedule's
+            # three kernels have none, so its traffic stays null.
+            on_blocks = (msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, dp.problem)
+                         == msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem))
             kernels.append(("msa_sparse_attn_prefill[%s]" % name, t_att, "mfma", alg["attn_flops"],
-                            ("attn_prefill.hip", "attn_prefill_tile", 1)))
+                            None if on_blocks else ("attn_prefill.hip", "attn_prefill_tile", 1, name)))
         results[name] = r
 
     kname, kms, kbound, kwork, ksrc = max(kernels, key=lambda x: x[1])
