@@ -53,76 +53,78 @@ __global__ __launch_bounds__(kScanThreads) void lists_block_offsets(const int32_
     }
 }
 
+// Key of selection element e = (row * h + g) * top_k + a: g * nb_max +
+// blk_off[s] + j for the block j in that slot, or -1 when the slot is empty or
+// the block is not visible to the row.  *entry receives row * top_k + a.
+// Threads take consecutive elements, so the reads of the ids (and of `place`)
+// are coalesced.
+__device__ __forceinline__ int selection_key(const int32_t *__restrict__ ids, long e,
+                                             const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
+                                             const int32_t *__restrict__ blk_off, int num_seqs, int h, int B,
+                                             int top_k, int nb_max, int *entry) {
+    const long pair = e / top_k;
+    const int a = (int)(e - pair * top_k);
+    const int row = (int)(pair / h), g = (int)(pair - (long)row * h);
+    *entry = row * top_k + a;
+    const int j = ids[e];
+    if (j < 0) return -1;
+    const int s = seq_of_row(cu_q, num_seqs, row);
+    const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
+    if (j > p / B) return -1;
+    return g * nb_max + blk_off[s] + j;
+}
+
 // Count (pass 0: each selection takes the next place of its key, kept in
-// `place`) or store (pass 1) every valid selection (row, g, block j) under key
-// g * nb_max + blk_off[s] + j; an entry is row * top_k + slot.
+// `place`) or store (pass 1) every valid selection element under its key; an
+// entry is row * top_k + slot.  Grid-stride over the n elements.
 template <int PASS>
 __global__ __launch_bounds__(256) void lists_invert(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
                                                   const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
-                                                  int num_seqs, int total_q, int h, int B, int top_k, int nb_max,
+                                                  int num_seqs, int h, int B, int top_k, int nb_max, long n,
                                                   int32_t *__restrict__ cnt, int32_t *__restrict__ place,
                                                   const int32_t *__restrict__ off, int32_t *__restrict__ entries) {
-    const long pair = (long)blockIdx.x * 256 + threadIdx.x;
-    if (pair >= (long)total_q * h) return;
-    const int row = (int)(pair / h), g = (int)(pair % h);
-    const int s = seq_of_row(cu_q, num_seqs, row);
-    const int len_q = cu_q[s + 1] - cu_q[s], len_k = cu_k[s + 1] - cu_k[s];
-    const int p = len_k - len_q + (row - cu_q[s]);
-    const int32_t *sel = ids + pair * top_k;
-    for (int a = 0; a < top_k; ++a) {
-        const int j = sel[a];
-        if (j < 0 || j > p / B) continue;
-        const long key = (long)g * nb_max + blk_off[s] + j;
+    for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
+        int entry;
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, &entry);
+        if (key < 0) continue;
         if (PASS == 0)
-            place[pair * top_k + a] = atomicAdd(&cnt[key], 1);
+            place[e] = atomicAdd(&cnt[key], 1);
         else
-            entries[off[key] + place[pair * top_k + a]] = row * top_k + a;
+            entries[off[key] + place[e]] = entry;
     }
 }
 
-// Pass 0 with the counting done in LDS first: the workgroup's selections take
-// local places in an LDS histogram of all keys, then each key the workgroup
-// touched takes one block of global places with a single atomic, so popular
-// blocks see one global atomic per workgroup instead of one per selection.
+// Pass 0 with the counting done in LDS first: the elements of one contiguous
+// chunk take local places in an LDS histogram of all keys, then each key the
+// chunk touched takes one block of global places with a single atomic, so
+// popular blocks see one global atomic per workgroup instead of one per
+// selection.
 constexpr int kHistKeys = 16384;  // largest key count this path handles (64 KB of LDS)
-__global__ __launch_bounds__(256) void lists_count_lds(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
+constexpr int kCountThreads = 1024;   // wide workgroups: the histogram's LDS caps how many fit on a CU
+__global__ __launch_bounds__(kCountThreads) void lists_count_lds(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
                                                      const int32_t *__restrict__ cu_k,
-                                                     const int32_t *__restrict__ blk_off, int num_seqs, int total_q,
-                                                     int h, int B, int top_k, int nb_max, int keys,
+                                                     const int32_t *__restrict__ blk_off, int num_seqs, int h, int B,
+                                                     int top_k, int nb_max, int keys, long n, long chunk,
                                                      int32_t *__restrict__ cnt, int32_t *__restrict__ place) {
     extern __shared__ int hist[];  // keys entries
-    for (int x = threadIdx.x; x < keys; x += 256) hist[x] = 0;
+    for (int x = threadIdx.x; x < keys; x += kCountThreads) hist[x] = 0;
     __syncthreads();
-    const long pair = (long)blockIdx.x * 256 + threadIdx.x;
-    const bool live = pair < (long)total_q * h;
-    int row = 0, g = 0, s = 0, p = -1;
-    if (live) {
-        row = (int)(pair / h);
-        g = (int)(pair % h);
-        s = seq_of_row(cu_q, num_seqs, row);
-        p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
-    }
-    const int32_t *sel = ids + pair * top_k;
-    if (live) {
-        for (int a = 0; a < top_k; ++a) {
-            const int j = sel[a];
-            if (j < 0 || j > p / B) continue;
-            const int key = g * nb_max + blk_off[s] + j;
-            place[pair * top_k + a] = atomicAdd(&hist[key], 1);
-        }
+    const long e0 = (long)blockIdx.x * chunk, e1 = e0 + chunk < n ? e0 + chunk : n;
+    for (long e = e0 + threadIdx.x; e < e1; e += kCountThreads) {
+        int entry;
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, &entry);
+        if (key >= 0) place[e] = atomicAdd(&hist[key], 1);
     }
     __syncthreads();
-    for (int x = threadIdx.x; x < keys; x += 256) {
+    for (int x = threadIdx.x; x < keys; x += kCountThreads) {
         const int c = hist[x];
         if (c > 0) hist[x] = atomicAdd(&cnt[x], c);
     }
     __syncthreads();
-    if (live) {
-        for (int a = 0; a < top_k; ++a) {
-            const int j = sel[a];
-            if (j < 0 || j > p / B) continue;
-            place[pair * top_k + a] += hist[g * nb_max + blk_off[s] + j];
-        }
+    for (long e = e0 + threadIdx.x; e < e1; e += kCountThreads) {
+        int entry;
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, &entry);
+        if (key >= 0) place[e] += hist[key];
     }
 }
 
@@ -189,22 +191,28 @@ hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLis
     int32_t *entries = reinterpret_cast<int32_t *>(base + w.entries);
     int32_t *place = reinterpret_cast<int32_t *>(base + w.place);
     const long keys = (long)s.h * w.nb_max;
-    const long pairs = (long)s.total_q * s.h;
-    auto grid_of = [](long n, long per) { return dim3((unsigned)((n + per - 1) / per)); };
+    const long n = (long)s.total_q * s.h * s.top_k;   // selection elements
+    auto grid_of = [](long m, long per) { return dim3((unsigned)((m + per - 1) / per)); };
     const dim3 zgrid = grid_of(std::min(keys, 1L << 22), 256);
+    const dim3 egrid = grid_of(std::min(n, 16384L * 256), 256);   // grid-stride over the elements
 
     hipLaunchKernelGGL(lists_block_offsets, dim3(1), dim3(kScanThreads), 0, st, s.cu_k, s.num_seqs, s.B, blk_off);
     hipLaunchKernelGGL(fill_zero_i32, zgrid, dim3(256), 0, st, cnt, keys);
-    if (keys <= kHistKeys)
-        hipLaunchKernelGGL(lists_count_lds, grid_of(pairs, 256), dim3(256), (size_t)keys * sizeof(int), st, ids,
-                           s.cu_q, s.cu_k, blk_off, s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max,
-                           (int)keys, cnt, place);
-    else
-        hipLaunchKernelGGL((lists_invert<0>), grid_of(pairs, 256), dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off,
-                           s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, cnt, place, nullptr, nullptr);
+    if (n > 0 && keys <= kHistKeys) {
+        // chunks of at least 4096 elements, at most 512 workgroups
+        const long wgs = std::min(512L, (n + 4095) / 4096);
+        const long chunk = ((n + wgs - 1) / wgs + kCountThreads - 1) / kCountThreads * kCountThreads;
+        hipLaunchKernelGGL(lists_count_lds, grid_of(n, chunk), dim3(kCountThreads), (size_t)keys * sizeof(int), st, ids, s.cu_q,
+                           s.cu_k, blk_off, s.num_seqs, s.h, s.B, s.top_k, (int)w.nb_max, (int)keys, n, chunk, cnt,
+                           place);
+    } else if (n > 0) {
+        hipLaunchKernelGGL((lists_invert<0>), egrid, dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off, s.num_seqs, s.h,
+                           s.B, s.top_k, (int)w.nb_max, n, cnt, place, nullptr, nullptr);
+    }
     hipLaunchKernelGGL(lists_scan, dim3(1), dim3(kScanThreads), 0, st, cnt, keys, off);
-    hipLaunchKernelGGL((lists_invert<1>), grid_of(pairs, 256), dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off,
-                       s.num_seqs, s.total_q, s.h, s.B, s.top_k, (int)w.nb_max, cnt, place, off, entries);
+    if (n > 0)
+        hipLaunchKernelGGL((lists_invert<1>), egrid, dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off, s.num_seqs, s.h,
+                           s.B, s.top_k, (int)w.nb_max, n, cnt, place, off, entries);
     return hipGetLastError();
 }
 
