@@ -257,12 +257,12 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
 }
 
 // O[row, head] and LSE from the partials of the row's valid slots, in one
-// pass.  One wave per (row, group), taking the group's G heads in turn (the
-// row's sequence lookup and ids are shared by them); lane = (slot lane group,
-// 16-byte chunk of a partial row), so every load instruction reads whole
-// partial rows.  Each lane merges its slots online (running max of their
-// log2-sum-exp, the sums rescaled when it grows), then the lanes' results are
-// brought to the wave's max and summed.
+// pass.  One wave per (row, group); lane = (head of the group, 16-byte chunk of
+// a partial row), 64 / (D / 8) heads per pass, so every load instruction
+// reads the contiguous partial rows of those heads for one slot.  Each lane
+// walks all the row's slots in order, merging online (running max of the
+// log2-sum-exp, the sums rescaled when it grows): every lane of a head holds
+// the same max and denominator, so no cross-lane reduction is needed.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ part_o, const float2 *__restrict__ part_w,
                                                  const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
@@ -270,26 +270,29 @@ __global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ pa
                                                  int h, int B, int top_k, uint16_t *__restrict__ out,
                                                  float *__restrict__ lse) {
     constexpr int CPR = D / 8;       // 16-byte chunks per partial row
-    constexpr int NSO = 64 / CPR;    // slot lane groups
-    const long rg = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int HPP = 64 / CPR;    // heads per pass
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const long rg = (long)blockIdx.x * 4 + wave;
     if (rg >= n_pairs) return;
-    const int lane = threadIdx.x & 63, c = lane % CPR, so = lane / CPR;
+    const int lane = threadIdx.x & 63, c = lane % CPR, hs = lane / CPR;
     const int row = (int)(rg / h), g = (int)(rg % h), G = H / h;
     const int s = seq_of_row(cu_q, num_seqs, row);
     const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
     const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
     const size_t base = (size_t)row * top_k;
 
-    for (int hh = 0; hh < G; ++hh) {
-        const int head = g * G + hh;
-        const size_t rh = (size_t)row * H + head;
+    for (int h0 = 0; h0 < G; h0 += HPP) {
+        const bool live = h0 + hs < G;
+        const int head = g * G + (live ? h0 + hs : 0);
         float m = -INFINITY, acc[8], den = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll 4
-        for (int a = so; a < top_k; a += NSO) {
+#pragma unroll 8
+        for (int a = 0; a < top_k; ++a) {
             const int j = sel[a];
-            const bool ok = j >= 0 && j <= p / B;
+            const bool ok = j >= 0 && j <= p / B;   // the same in every lane
+            // the loads are unconditional (slot 0's row stands in for a
+            // skipped slot) so that the unrolled slots' loads overlap
             const size_t sh = (base + (ok ? a : 0)) * H + head;
             const float2 w = part_w[sh];
             const uint4 x = load16(part_o + sh * D + 8 * c);
@@ -305,26 +308,13 @@ __global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ pa
                 m = m_new;
             }
         }
-        // bring every lane to the wave's max, then sum the slot lane groups
-        float mw = m;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o, 64));
-        const float scale = m == -INFINITY ? 0.f : fast_exp2(m - mw);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= scale;
-        den = c == 0 ? den * scale : 0.f;   // one copy of each slot's weight per slot lane group
-#pragma unroll
-        for (int o = CPR; o < 64; o <<= 1)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o, 64);
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o, 64);
         const float inv = den > 0.f ? 1.0f / den : 0.f;
-        if (so == 0)
+        const size_t rh = (size_t)row * H + head;
+        if (live)
             *reinterpret_cast<uint4 *>(out + rh * D + 8 * c) =
                 uint4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                       pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-        if (lse != nullptr && lane == 0) lse[rh] = den > 0.f ? (mw + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+        if (lse != nullptr && live && c == 0) lse[rh] = den > 0.f ? (m + __log2f(den)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
