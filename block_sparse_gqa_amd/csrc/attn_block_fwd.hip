@@ -378,7 +378,7 @@ bool prefill_prefers_blocks(const Shape &s) {
     const double e_k = (double)((s.max_k + s.B - 1) / s.B), e_q = (double)((s.max_q + s.B - 1) / s.B);
     const double e_avg = std::max(1.0, e_k - 0.5 * e_q);
     const double r = (double)prefill_tile_queries(s) * std::min((double)s.top_k, e_k) / e_avg;
-    return r < (s.B >= 128 ? 9.0 : 5.0);
+    return r < (s.B >= 128 ? 10.0 : 7.0);
 }
 
 hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
