@@ -366,11 +366,13 @@ size_t block_prefill_workspace_bytes(const Shape &s) { return fwd_ws(s).bytes; }
 // R = Tq k / E_avg of them, with Tq queries per tile and E_avg the eligible
 // blocks of an average query of the longest sequence.  The block-centric
 // schedule does no wasted work but writes and reads back one partial output
-// per (row, slot, head).  Measured on the 32K-131K-token prefills
-// (query tiles / block-centric time): B = 64, G = 4 gave 0.40, 0.50, 0.70,
-// 1.05, 1.23 at R = 32, 16, 8, 4, 2; B = 128, G = 6 gave 0.49, 0.77, 1.14,
-// 1.65 at R = 16, 8, 4, 2 and 5.4 at about 1 (the 4-sequence 217K ragged
-// prefill).  The switch points are R = 4 (B = 64) and R = 6 (B = 128).
+// per (row, slot, head).  Measured on 8K-64K-token prefills with clustered
+// keys, each schedule called on its own (query-tile time / block-centric
+// time): B = 64, G = 4 gave 0.48 at R = 32, 0.71-0.72 at 16, 0.92-0.96 at 8,
+// 1.10 at 6, 1.31-1.32 at 4 and 1.68 at 2; B = 128, G = 6 gave 0.65 at
+// R = 16, 0.89 at 12, 1.05 at 8, 1.22 at 6, 1.49 at 4, 2.13 at 2 and about
+// 7 at about 1 (a 4-sequence 217K-token ragged prefill).  So the switch
+// points are R = 7 (B = 64) and R = 10 (B = 128).
 bool prefill_prefers_blocks(const Shape &s) {
     const int G = s.H / s.h;
     if (G < 1 || G > 16 || s.max_q < 1) return false;
