@@ -8,9 +8,15 @@ One step = one pass of the whole hot path over the two headline workloads:
     clustered keys  (msa_index_topk + msa_sparse_attn_prefill)
 Inputs are seeded synthetic bf16 tensors, resident in HBM before timing starts.
 
+The other three configurations (the tiny prefill, decode at 64K context and
+the ragged 4-sequence prefill) are then timed on their own and reported in
+`results` beside the headline; they are not part of `value`.
+
 Prints one JSON line: whole-step tokens/s, per-workload results, the roofline
 of the dominant kernel (algorithmic bytes or flops per launch over its HIP-event
-duration) and the CPU oracle timed on a bounded sample of the same step.
+duration) and the CPU leg: the oracle timed on a bounded sample of the same
+step, and every workload's top-k ids checked against the oracle's on sampled
+rows (near ties and in-band flips counted, per workload).
 """
 from __future__ import annotations
 
@@ -30,6 +36,9 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MSA tokens/s: decode@1M ctx & prefill@32k; % of HBM/MFMA roofline"
 WORKLOADS = ("decode_1m", "prefill_32k")
+# The other three configurations: each timed on its own after the step, reported beside the
+# headline (not part of `value`).
+EXTRA_WORKLOADS = ("tiny_prefill", "decode_64k", "ragged_prefill")
 
 
 def log(*a):
@@ -66,6 +75,42 @@ def algorithmic(inp, dp, ids):
     attn_bytes = float(tok_sel * d * 2 * 2 + 2 * wl.total_q * H * d * 2 + wl.total_q * h * wl.top_k * 4)
     return dict(index_flops=index_flops, attn_flops=attn_flops, index_bytes=index_bytes, attn_bytes=attn_bytes,
                 selected_tokens=tok_sel)
+
+
+def cpu_model():
+    """The host CPU's model name and logical CPU count, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            names = [l.split(":", 1)[1].strip() for l in f if l.startswith("model name")]
+    except OSError:
+        names = []
+    return {"model": names[0] if names else "unknown", "logical_cpus": len(names) or (os.cpu_count() or 0)}
+
+
+def selection_parity(inputs, gpu_ids, seed=9):
+    """Top-k ids of every workload against the oracle's on sampled rows, with the near-tie rule:
+    near-tie pairs, in-band flips and exact mismatches (pairs differing outside the band)."""
+    import oracle
+    from block_sparse_gqa_amd import synth
+    from tests import parity
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    res = {}
+    for name, inp in inputs.items():
+        wl = inp.wl
+        if wl.is_decode or wl.total_q <= 1024:
+            rows = np.arange(wl.total_q, dtype=np.int64)
+            what = "every row"
+        else:
+            rows = synth.sample_rows(wl, n_per_seq=96, seed=seed)
+            what = "sampled rows (block edges, sequence ends, seeded random)"
+        t0 = time.perf_counter()
+        ref_ids, kth, tie = oracle.index_topk(inp, rows, threads=threads)
+        rep = parity.selection_report(oracle, inp, rows, gpu_ids[name][rows], ref_ids, kth, tie)
+        rep.update({"rows_checked": what, "oracle_s": time.perf_counter() - t0})
+        res[name] = rep
+        log(f"[bench] selection parity {name}: {rep}")
+    return res
 
 
 def cpu_baseline(inputs, budget_s=24.0, seed=7):
@@ -105,6 +150,7 @@ def cpu_baseline(inputs, budget_s=24.0, seed=7):
         parts.append(f"{name}: {done} of {wl.total_q} {what} in {dt:.1f} s")
     tokens = sum(inp.wl.total_q for inp in inputs.values())
     return {"value": tokens / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": "; ".join(parts) + "; each part extrapolated linearly to its full workload"}
 
 
@@ -277,6 +323,86 @@ def prefill_schedules(dp, bufs, fwd, steps):
     return res
 
 
+def summarize(inp, dp, ids, evs):
+    """Per-workload result from the events of its timed calls: (index start, index end = attention
+    start, attention end) per step.  Returns the result dict and the (name, ms, bound, work, counters)
+    entries of its two calls for the roofline."""
+    from block_sparse_gqa_amd import msa
+    wl, name = inp.wl, inp.wl.name
+    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    per_step = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    alg = algorithmic(inp, dp, ids)
+    kernels = []
+    r = {"tokens": wl.total_q, "ms": t_idx + t_att, "tokens_per_s": wl.total_q / ((t_idx + t_att) * 1e-3),
+         "ms_median": float(np.median(per_step)), "ms_min": float(per_step.min()),
+         "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "selected_tokens": alg["selected_tokens"],
+         "workload": wl.description}
+    if wl.is_decode:
+        gbs_i = alg["index_bytes"] / (t_idx * 1e-3) / 1e9
+        gbs_a = alg["attn_bytes"] / (t_att * 1e-3) / 1e9
+        tot = (alg["index_bytes"] + alg["attn_bytes"]) / ((t_idx + t_att) * 1e-3) / 1e9
+        r.update({"bound": "hbm", "algorithmic_GB": (alg["index_bytes"] + alg["attn_bytes"]) / 1e9,
+                  "GB_per_s": tot, "frac_hbm_peak": tot / HBM_PEAK_GBS,
+                  "index_topk_GB_per_s": gbs_i, "sparse_attn_GB_per_s": gbs_a})
+        kernels.append(("msa_index_topk[%s]" % name, t_idx, "hbm", alg["index_bytes"], None))
+        kernels.append(("msa_sparse_attn_decode[%s]" % name, t_att, "hbm", alg["attn_bytes"], None))
+    else:
+        tf_i = alg["index_flops"] / (t_idx * 1e-3) / 1e12
+        tf_a = alg["attn_flops"] / (t_att * 1e-3) / 1e12
+        tot = (alg["index_flops"] + alg["attn_flops"]) / ((t_idx + t_att) * 1e-3) / 1e12
+        on_blocks = (msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, dp.problem)
+                     == msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem))
+        r.update({"bound": "mfma", "algorithmic_TFLOP": (alg["index_flops"] + alg["attn_flops"]) / 1e12,
+                  "TFLOP_per_s": tot, "frac_mfma_peak": tot / MFMA_BF16_PEAK_TFLOPS,
+                  "index_topk_TFLOP_per_s": tf_i, "sparse_attn_TFLOP_per_s": tf_a,
+                  "index_topk_frac_mfma_peak": tf_i / MFMA_BF16_PEAK_TFLOPS,
+                  "sparse_attn_frac_mfma_peak": tf_a / MFMA_BF16_PEAK_TFLOPS,
+                  "prefill_schedule": "blocks" if on_blocks else "tiles"})
+        kernels.append(("msa_index_topk[%s]" % name, t_idx, "mfma", alg["index_flops"], None))
+        # One launch of attn_prefill_tile per call on the query-tile schedule.  The committed
+        # counters cover that kernel on the workloads they name; the block-centric schedule's
+        # three kernels have none, so its traffic stays null.
+        kernels.append(("msa_sparse_attn_prefill[%s]" % name, t_att, "mfma", alg["attn_flops"],
+                        None if on_blocks else ("attn_prefill.hip", "attn_prefill_tile", 1, name)))
+    return r, kernels
+
+
+def time_extra(name, steps, warmup):
+    """One of the other configurations, timed on its own: `warmup` untimed and `steps` timed passes of
+    index_topk + attention, then (decode) flushed repetitions.  Frees its device memory before it
+    returns; gives back the inputs and the GPU's ids (host) for the selection check."""
+    import torch
+
+    from block_sparse_gqa_amd import device, synth
+    log(f"[bench] generating {name}")
+    inp = synth.make_inputs(name)
+    dp = device.upload(inp)
+    ids = device.alloc_ids(dp)
+    out, lse = device.alloc_out(dp)
+    for _ in range(warmup):
+        device.index_topk(dp, ids)
+        device.sparse_attention(dp, ids, out, lse)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record()
+        device.index_topk(dp, ids)
+        e[1].record()
+        device.sparse_attention(dp, ids, out, lse)
+        e[2].record()
+    torch.cuda.synchronize()
+    r, _ = summarize(inp, dp, ids, evs)
+    if inp.wl.is_decode:
+        r["flushed_reps"] = decode_reps(dp, (ids, out, lse))
+        r["flushed_reps"]["GB_per_s_median"] = r["algorithmic_GB"] / (r["flushed_reps"]["ms_median"] * 1e-3)
+    host_ids = ids.cpu().numpy()
+    del dp, ids, out, lse
+    torch.cuda.empty_cache()
+    log(f"[bench] {name}: {r['ms']:.3f} ms")
+    return r, inp, host_ids
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +416,8 @@ def main():
                     help="skip timing both prefill schedules explicitly (reported beside the headline)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement (reported beside the headline, not in it)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip timing the other three configurations (reported beside the headline, not in it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -354,43 +482,10 @@ def main():
     results, kernels = {}, []
     total_tokens = 0
     for name in names:
-        inp, dp = inputs[name], dps[name]
-        ids = bufs[name][0]
-        t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[name]]))
-        t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in ev[name]]))
-        per_step = np.array([e[0].elapsed_time(e[2]) for e in ev[name]])
-        alg = algorithmic(inp, dp, ids)
-        wl = inp.wl
-        total_tokens += wl.total_q
-        r = {"tokens": wl.total_q, "ms": t_idx + t_att, "tokens_per_s": wl.total_q / ((t_idx + t_att) * 1e-3),
-             "ms_median": float(np.median(per_step)), "ms_min": float(per_step.min()),
-             "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "selected_tokens": alg["selected_tokens"],
-             "workload": wl.description}
-        if wl.is_decode:
-            gbs_i = alg["index_bytes"] / (t_idx * 1e-3) / 1e9
-            gbs_a = alg["attn_bytes"] / (t_att * 1e-3) / 1e9
-            tot = (alg["index_bytes"] + alg["attn_bytes"]) / ((t_idx + t_att) * 1e-3) / 1e9
-            r.update({"bound": "hbm", "algorithmic_GB": (alg["index_bytes"] + alg["attn_bytes"]) / 1e9,
-                      "GB_per_s": tot, "frac_hbm_peak": tot / HBM_PEAK_GBS,
-                      "index_topk_GB_per_s": gbs_i, "sparse_attn_GB_per_s": gbs_a})
-            kernels.append(("msa_index_topk[%s]" % name, t_idx, "hbm", alg["index_bytes"], None))
-            kernels.append(("msa_sparse_attn_decode[%s]" % name, t_att, "hbm", alg["attn_bytes"], None))
-        else:
-            tf_i = alg["index_flops"] / (t_idx * 1e-3) / 1e12
-            tf_a = alg["attn_flops"] / (t_att * 1e-3) / 1e12
-            tot = (alg["index_flops"] + alg["attn_flops"]) / ((t_idx + t_att) * 1e-3) / 1e12
-            r.update({"bound": "mfma", "algorithmic_TFLOP": (alg["index_flops"] + alg["attn_flops"]) / 1e12,
-                      "TFLOP_per_s": tot, "frac_mfma_peak": tot / MFMA_BF16_PEAK_TFLOPS,
-                      "index_topk_TFLOP_per_s": tf_i, "sparse_attn_TFLOP_per_s": tf_a})
-            kernels.append(("msa_index_topk[%s]" % name, t_idx, "mfma", alg["index_flops"], None))
-            # One launch of attn_prefill_tile per call on the query-tile schedule.  The committed
-            # counters cover that kernel on the workloads they name; the block-centric schedule's
-            # three kernels have none, so its traffic stays null.
-            on_blocks = (msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, dp.problem)
-                         == msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem))
-            kernels.append(("msa_sparse_attn_prefill[%s]" % name, t_att, "mfma", alg["attn_flops"],
-                            None if on_blocks else ("attn_prefill.hip", "attn_prefill_tile", 1, name)))
+        r, ks = summarize(inputs[name], dps[name], bufs[name][0], ev[name])
+        total_tokens += inputs[name].wl.total_q
         results[name] = r
+        kernels.extend(ks)
 
     kname, kms, kbound, kwork, ksrc = max(kernels, key=lambda x: x[1])
     if kbound == "hbm":
@@ -424,6 +519,14 @@ def main():
             if inputs[name].wl.is_decode:
                 results[name]["paged"] = paged_decode(inputs[name], dps[name], bufs[name][0], results[name],
                                                       max(args.steps, 5), args.warmup)
+
+    host_ids = {n: bufs[n][0].cpu().numpy() for n in names}
+    extra_inputs = {}
+    if not args.no_extra:
+        for name in EXTRA_WORKLOADS:
+            if name in names:
+                continue
+            results[name], extra_inputs[name], host_ids[name] = time_extra(name, args.steps, args.warmup)
 
     # achievable HBM rate on this GPU: a plain 4 GiB device-to-device copy (read + write)
     src = torch.empty(1 << 32, dtype=torch.uint8, device="cuda")
@@ -464,8 +567,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        # the CPU leg: the oracle timed on a bounded sample of the step, and the GPU's ids of every
+        # workload checked against the oracle's on sampled rows (near ties counted)
         log("[bench] timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(inputs)
+        for name, rep in selection_parity({**inputs, **extra_inputs}, host_ids).items():
+            results[name]["selection_parity"] = rep
 
     line = {
         "metric": METRIC,
@@ -481,7 +588,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) / clustered-block bf16 inputs, generated on the host)",
         "config": {"workload": " + ".join(names), "parallelism": "single GPU",
-                   **{n: results[n]["workload"] for n in names}},
+                   **{n: results[n]["workload"] for n in names},
+                   "also_reported": [n for n in results if n not in names]},
         "results": results,
         "roofline": roofline,
         "ceilings": {"hbm_copy_GB_per_s": copy_gbs, "hbm_stream_read_GB_per_s": read_gbs,

@@ -36,6 +36,8 @@
 //                     the S^T accumulators.
 // Workgroups are numbered group-fastest, so with 8 groups all tiles of a
 // group run on the same XCD and share its L2.
+#include <cstdlib>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -48,7 +50,10 @@ typedef __attribute__((address_space(1))) void gbl_void;
 
 constexpr int kWin = 256;    // key blocks per union window (one per thread)
 constexpr int kStages = 4;   // ring depth (sub-blocks)
-// Upper bound on polls of one ready stamp (each poll sleeps ~64 cycles).
+// Default bound on polls of one ready stamp (each poll sleeps ~64 cycles,
+// so about 30 ms at 2.4 GHz: far above any wait of a working protocol).  A
+// wait that reaches the bound counts itself in the workspace's wait word and
+// goes on; the call's output is then not valid.
 constexpr int kSpinLimit = 1 << 20;
 // Fourth word of a raw buffer resource (32-bit data format, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
     int num_seqs, int H, int h, int B, int top_k, int max_tiles, float c2, const int *__restrict__ v_exp,
-    uint16_t *__restrict__ out, float *__restrict__ lse) {
+    uint16_t *__restrict__ out, float *__restrict__ lse, int spin_limit, unsigned *__restrict__ wait_flag) {
     using R = Ring<D>;
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
@@ -512,13 +517,22 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
                     const int t0 = blk * B + sub * 64;
                     if (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) != it + 1) {
                         publish();
-                        // bounded (kSpinLimit polls, tens of milliseconds, far above any
-                        // real wait): a broken protocol would end the kernel with wrong
-                        // results instead of hanging the device
-                        for (int spin = 0; spin < kSpinLimit; ++spin) {
-                            if (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) == it + 1) break;
+                        // bounded (spin_limit polls): a wait that never ends
+                        // would hang the device, so one that reaches the bound
+                        // is counted in the wait word and the item is attended
+                        // as the stage holds it (the output is then invalid,
+                        // and the caller can see it)
+                        bool ready_now = false;
+                        for (int spin = 0; spin < spin_limit; ++spin) {
+                            if (__builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) == it + 1) {
+                                ready_now = true;
+                                break;
+                            }
                             __builtin_amdgcn_s_sleep(1);
                         }
+                        if (!ready_now)
+                            ready_now = __builtin_amdgcn_readfirstlane(lds_u32(ready0 + 4 * stage)) == it + 1;
+                        if (!ready_now && lane == 0) atomicAdd(wait_flag, 1u);
                     }
                     const uint32_t sbase = ring0 + stage * R::STAGE;
                     if (t0 <= p_wave_last) {
@@ -591,7 +605,8 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float mul) {
 
 __global__ __launch_bounds__(256) void v_to_f16(const uint4 *__restrict__ v, long n16,
                                                 const uint32_t *__restrict__ part, int nparts,
-                                                uint4 *__restrict__ v16, int *__restrict__ v_exp) {
+                                                uint4 *__restrict__ v16, int *__restrict__ v_exp,
+                                                unsigned *__restrict__ wait_flag) {
     uint32_t m = 0;
     for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, part[i]);
 #pragma unroll
@@ -604,7 +619,10 @@ __global__ __launch_bounds__(256) void v_to_f16(const uint4 *__restrict__ v, lon
     // puts it in [2^14, 2^15) whatever its magnitude (2^-e stays a normal
     // float).  Infinities and NaN keep e = 0 and pass through as such.
     const int e = (m >= 0x7f80u) ? 0 : max(-126, (int)(m >> 7) - 141);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *v_exp = e;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *v_exp = e;
+        *wait_flag = 0u;   // the attention kernel that follows counts its given-up waits here
+    }
     const float mul = __builtin_ldexpf(1.0f, -e);
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256) {
         const uint4 x = v[i];
@@ -613,8 +631,11 @@ __global__ __launch_bounds__(256) void v_to_f16(const uint4 *__restrict__ v, lon
     }
 }
 
+// Workspace: the fp16 copy of V, the max pass's partial maxima, then one
+// 256-byte slot holding the scale exponent (word 0) and the wait word
+// (word 1, the count of ring waits that reached their bound in the last call).
 struct PrefillWs {
-    size_t v16_off, part_off, exp_off, bytes;
+    size_t v16_off, part_off, exp_off, flag_off, bytes;
 };
 PrefillWs prefill_ws(const Shape &s) {
     PrefillWs w;
@@ -622,26 +643,41 @@ PrefillWs prefill_ws(const Shape &s) {
     w.v16_off = 0;
     w.part_off = (vb + 255) / 256 * 256;
     w.exp_off = w.part_off + kCvtParts * sizeof(uint32_t);
+    w.flag_off = w.exp_off + sizeof(int);
     w.bytes = w.exp_off + 256;
     return w;
 }
 
+// Polls per ring wait: kSpinLimit, or MSA_DEBUG_SPIN_LIMIT when that is set
+// to a non-negative integer (a debugging aid: a tiny bound makes the waits
+// give up, so the wait word can be seen to work; every kernel still ends).
+int spin_limit_from_env() {
+    const char *e = getenv("MSA_DEBUG_SPIN_LIMIT");
+    if (e == nullptr || *e == 0) return kSpinLimit;
+    char *end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (*end != 0 || v < 0) return kSpinLimit;
+    return v > kSpinLimit ? kSpinLimit : (int)v;
+}
+
 template <int D, int NW>
 hipError_t launch(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v16, const int *v_exp,
-                  const int32_t *ids, float scale, uint16_t *out, float *lse, hipStream_t st) {
+                  const int32_t *ids, float scale, uint16_t *out, float *lse, unsigned *wait_flag, hipStream_t st) {
     const int G = s.H / s.h;
     const int Tq = NW * (16 / G);
     const int max_tiles = (s.max_q + Tq - 1) / Tq;
     const long grid = (long)max_tiles * s.num_seqs * s.h;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_prefill_tile<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, q, k, v16, ids, s.cu_q,
-                       s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, v_exp, out, lse);
+                       s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, v_exp, out, lse,
+                       spin_limit_from_env(), wait_flag);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t prefill_workspace_bytes(const Shape &s) { return prefill_ws(s).bytes; }
+size_t prefill_wait_word_offset(const Shape &s) { return prefill_ws(s).flag_off; }
 
 int prefill_tile_queries(const Shape &s) {
     // One 16-row tile per wave, as many waves as keep the tile within 64
@@ -665,24 +701,25 @@ hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t
     uint16_t *v16 = reinterpret_cast<uint16_t *>(wsb + w.v16_off);
     uint32_t *part = reinterpret_cast<uint32_t *>(wsb + w.part_off);
     int *v_exp = reinterpret_cast<int *>(wsb + w.exp_off);
+    unsigned *wait_flag = reinterpret_cast<unsigned *>(wsb + w.flag_off);
     const long n16 = (long)s.total_k * s.h * s.d / 8;
     const long need = (n16 + 255) / 256;
     const int nparts = (int)(need < kCvtParts ? need : kCvtParts);
     hipLaunchKernelGGL(v_absmax_bits, dim3(nparts), dim3(256), 0, st, reinterpret_cast<const uint4 *>(v), n16, part);
     const int ncvt = (int)(need < 4096 ? need : 4096);
     hipLaunchKernelGGL(v_to_f16, dim3(ncvt), dim3(256), 0, st, reinterpret_cast<const uint4 *>(v), n16, part, nparts,
-                       reinterpret_cast<uint4 *>(v16), v_exp);
+                       reinterpret_cast<uint4 *>(v16), v_exp, wait_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nw = prefill_tile_queries(s) / (16 / G);
     if (s.d == 64) {
-        if (nw == 16) return launch<64, 16>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
-        if (nw == 8) return launch<64, 8>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
-        return launch<64, 4>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
+        if (nw == 16) return launch<64, 16>(s, q, k, v16, v_exp, ids, scale, out, lse, wait_flag, st);
+        if (nw == 8) return launch<64, 8>(s, q, k, v16, v_exp, ids, scale, out, lse, wait_flag, st);
+        return launch<64, 4>(s, q, k, v16, v_exp, ids, scale, out, lse, wait_flag, st);
     }
-    if (nw == 16) return launch<128, 16>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
-    if (nw == 8) return launch<128, 8>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
-    return launch<128, 4>(s, q, k, v16, v_exp, ids, scale, out, lse, st);
+    if (nw == 16) return launch<128, 16>(s, q, k, v16, v_exp, ids, scale, out, lse, wait_flag, st);
+    if (nw == 8) return launch<128, 8>(s, q, k, v16, v_exp, ids, scale, out, lse, wait_flag, st);
+    return launch<128, 4>(s, q, k, v16, v_exp, ids, scale, out, lse, wait_flag, st);
 }
 
 }  // namespace msa

@@ -3,7 +3,9 @@
 // frees or synchronises; every check runs on the host before any launch.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <new>
+#include <vector>
 
 #include "msa.h"
 #include "msa_internal.h"
@@ -78,6 +80,18 @@ msa_status_t check_ws(void *ws, size_t have, size_t need) {
 
 msa_status_t launched(hipError_t e) { return e == hipSuccess ? MSA_SUCCESS : MSA_ERROR_LAUNCH; }
 
+// The debug mode: with MSA_DEBUG_VALIDATE set to a non-empty value other than
+// "0", the entry points copy cu_seqlens (and the ids they read) to the host,
+// waiting for the copies, and check them with msa_validate_host before
+// launching anything.
+bool debug_validate_on() {
+    const char *e = getenv("MSA_DEBUG_VALIDATE");
+    return e != nullptr && *e != 0 && !(e[0] == '0' && e[1] == 0);
+}
+
+msa_status_t debug_validate(const msa_problem_t &p, const int32_t *ids, hipStream_t st);
+
+
 }  // namespace
 
 extern "C" {
@@ -123,6 +137,60 @@ size_t msa_workspace_size(int op, const msa_problem_t *problem) {
     return (size_t)-1;
 }
 
+msa_status_t msa_validate_host(const msa_problem_t *problem, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_k, const int32_t *topk_ids) {
+    if (problem == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return MSA_ERROR_INVALID_VALUE;
+    const msa_problem_t &p = *problem;
+    if (p.num_seqs < 1 || p.total_q < 0 || p.total_k < 0 || p.num_kv_heads < 1 || p.block_size < 1 || p.top_k < 1)
+        return MSA_ERROR_INVALID_VALUE;
+    const int n = p.num_seqs;
+    if (cu_seqlens_q[0] != 0 || cu_seqlens_k[0] != 0) return MSA_ERROR_INVALID_VALUE;
+    if (cu_seqlens_q[n] != p.total_q || cu_seqlens_k[n] != p.total_k) return MSA_ERROR_INVALID_VALUE;
+    for (int i = 0; i < n; ++i) {
+        const long lq = (long)cu_seqlens_q[i + 1] - cu_seqlens_q[i];
+        const long lk = (long)cu_seqlens_k[i + 1] - cu_seqlens_k[i];
+        if (lq < 0 || lk < 0 || lk < lq) return MSA_ERROR_INVALID_VALUE;
+        if (lq > p.max_seqlen_q || lk > p.max_seqlen_k) return MSA_ERROR_INVALID_VALUE;
+    }
+    if (topk_ids == nullptr) return MSA_SUCCESS;
+    const int h = p.num_kv_heads, k = p.top_k;
+    std::vector<unsigned char> seen;
+    for (int i = 0; i < n; ++i) {
+        const int lq = cu_seqlens_q[i + 1] - cu_seqlens_q[i];
+        const int lk = cu_seqlens_k[i + 1] - cu_seqlens_k[i];
+        for (int r = 0; r < lq; ++r) {
+            const long E = (long)(lk - lq + r) / p.block_size + 1;
+            seen.assign((size_t)E, 0);
+            const int32_t *row = topk_ids + ((size_t)(cu_seqlens_q[i] + r) * h) * k;
+            for (int g = 0; g < h; ++g) {
+                for (int a = 0; a < k; ++a) {
+                    const int32_t j = row[(size_t)g * k + a];
+                    if (j == -1) continue;
+                    if (j < 0 || j >= E) return MSA_ERROR_INVALID_VALUE;
+                    if (seen[(size_t)j] == (unsigned char)(g + 1)) return MSA_ERROR_INVALID_VALUE;
+                    seen[(size_t)j] = (unsigned char)(g + 1);
+                }
+            }
+        }
+    }
+    return MSA_SUCCESS;
+}
+
+size_t msa_workspace_wait_word(int op, const msa_problem_t *problem) {
+    if (check_problem(problem) != MSA_SUCCESS) return (size_t)-1;
+    const msa_problem_t &p = *problem;
+    if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
+    const Shape s = to_shape(p);
+    switch (op) {
+        case MSA_OP_SPARSE_ATTN_PREFILL:
+            if (msa::prefill_prefers_blocks(s)) return (size_t)-1;
+            return msa::prefill_wait_word_offset(s);
+        case MSA_OP_SPARSE_ATTN_PREFILL_TILES:
+            return msa::prefill_wait_word_offset(s);
+    }
+    return (size_t)-1;
+}
+
 msa_status_t msa_index_topk(const msa_problem_t *problem, const msa_bf16_t *q_idx, const msa_bf16_t *k_idx,
                             int32_t *topk_ids, void *workspace, size_t workspace_bytes, msa_stream_t stream) {
     return msa_index_topk_ex(problem, nullptr, nullptr, q_idx, k_idx, topk_ids, workspace, workspace_bytes, stream);
@@ -147,6 +215,7 @@ msa_status_t prefill_call(Schedule which, const msa_problem_t *problem, const ms
     if (which == Schedule::kBlocks && (long long)p.total_q * p.top_k > 0x7fffffffLL) return MSA_ERROR_NOT_SUPPORTED;
     const bool blocks = which == Schedule::kBlocks || (which == Schedule::kAuto && msa::prefill_prefers_blocks(s));
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (debug_validate_on() && (st = debug_validate(p, topk_ids, hs)) != MSA_SUCCESS) return st;
     if (blocks) {
         if ((st = check_ws(workspace, workspace_bytes, msa::block_prefill_workspace_bytes(s))) != MSA_SUCCESS)
             return st;
@@ -197,6 +266,9 @@ msa_status_t msa_sparse_attn_prefill_backward(const msa_problem_t *problem, cons
     if ((st = attn_support(p)) != MSA_SUCCESS) return st;
     Shape s = to_shape(p);
     if ((st = check_ws(workspace, workspace_bytes, msa::backward_workspace_bytes(s))) != MSA_SUCCESS) return st;
+    if (debug_validate_on() &&
+        (st = debug_validate(p, topk_ids, reinterpret_cast<hipStream_t>(stream))) != MSA_SUCCESS)
+        return st;
     return launched(msa::launch_attn_backward(s, q, k, v, topk_ids, softmax_scale, out, lse, dout, dq, dk, dv,
                                               workspace, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -216,6 +288,9 @@ msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16
     if ((st = attn_support(p)) != MSA_SUCCESS) return st;
     Shape s = to_shape(p);
     if ((st = check_ws(workspace, workspace_bytes, msa::decode_workspace_bytes(s))) != MSA_SUCCESS) return st;
+    if (debug_validate_on() &&
+        (st = debug_validate(p, topk_ids, reinterpret_cast<hipStream_t>(stream))) != MSA_SUCCESS)
+        return st;
     return launched(msa::launch_attn_decode(s, q, k_cache, v_cache, topk_ids, softmax_scale, out, lse, workspace,
                                             reinterpret_cast<hipStream_t>(stream)));
 }
@@ -268,9 +343,15 @@ msa_status_t msa_index_topk_ex(const msa_problem_t *problem, const msa_select_op
         s.local = options->local_blocks;
     }
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (debug_validate_on() && (st = debug_validate(p, nullptr, hs)) != MSA_SUCCESS) return st;
     float *scores = reinterpret_cast<float *>(workspace);
-    hipError_t e = (p.max_seqlen_q == 1) ? msa::launch_index_decode(s, q_idx, k_idx, scores, hs)
-                                         : msa::launch_index_prefill(s, q_idx, k_idx, scores, hs);
+    // The decode scan takes the last query of every sequence, so it needs
+    // exactly one query per sequence; a batch with empty sequences (fewer
+    // queries than sequences) goes through the prefill kernel, which skips
+    // them.  (The paged path has already required total_q == num_seqs.)
+    const bool decode = p.max_seqlen_q == 1 && p.total_q == p.num_seqs;
+    hipError_t e = decode ? msa::launch_index_decode(s, q_idx, k_idx, scores, hs)
+                          : msa::launch_index_prefill(s, q_idx, k_idx, scores, hs);
     if (e != hipSuccess) return MSA_ERROR_LAUNCH;
     return launched(msa::launch_topk_select(s, scores, topk_ids, hs));
 }
@@ -291,6 +372,9 @@ msa_status_t msa_sparse_attn_decode_paged(const msa_problem_t *problem, const ms
     Shape s = to_shape(p);
     if ((st = check_ws(workspace, workspace_bytes, msa::decode_workspace_bytes(s))) != MSA_SUCCESS) return st;
     set_paged(s, *paged);
+    if (debug_validate_on() &&
+        (st = debug_validate(p, topk_ids, reinterpret_cast<hipStream_t>(stream))) != MSA_SUCCESS)
+        return st;
     return launched(msa::launch_attn_decode(s, q, k_pool, v_pool, topk_ids, softmax_scale, out, lse, workspace,
                                             reinterpret_cast<hipStream_t>(stream)));
 }
@@ -346,3 +430,22 @@ msa_status_t msa_ceiling_mfma_bf16(int32_t iterations, float *sink, double *flop
 }
 
 }  // extern "C"
+
+namespace {
+
+msa_status_t debug_validate(const msa_problem_t &p, const int32_t *ids, hipStream_t st) {
+    std::vector<int32_t> cq((size_t)p.num_seqs + 1), ck((size_t)p.num_seqs + 1), hid;
+    const size_t cu_bytes = cq.size() * sizeof(int32_t);
+    if (hipMemcpyAsync(cq.data(), p.cu_seqlens_q, cu_bytes, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipMemcpyAsync(ck.data(), p.cu_seqlens_k, cu_bytes, hipMemcpyDeviceToHost, st) != hipSuccess)
+        return MSA_ERROR_LAUNCH;
+    if (ids != nullptr) {
+        hid.resize((size_t)p.total_q * p.num_kv_heads * p.top_k);
+        if (hipMemcpyAsync(hid.data(), ids, hid.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+            return MSA_ERROR_LAUNCH;
+    }
+    if (hipStreamSynchronize(st) != hipSuccess) return MSA_ERROR_LAUNCH;
+    return msa_validate_host(&p, cq.data(), ck.data(), ids != nullptr ? hid.data() : nullptr);
+}
+
+}  // namespace

@@ -37,6 +37,9 @@ int max_select_blocks();
 
 // Sparse branch.
 size_t prefill_workspace_bytes(const Shape &s);
+// Byte offset in that workspace of the uint32 wait word (ring waits that
+// reached their bound in the last call; 0 = none).
+size_t prefill_wait_word_offset(const Shape &s);
 hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                hipStream_t st);

@@ -91,6 +91,20 @@ def sparse_attention_tiles(dp: DeviceProblem, ids, out=None, lse=None, ws=None, 
     return out, lse
 
 
+def workspace(dp: DeviceProblem, op: int):
+    """A workspace of the size the entry point `op` needs for this problem (None if it needs none)."""
+    return _workspace(op, dp.problem, dp.q.device)
+
+
+def wait_word(dp: DeviceProblem, op: int, ws) -> int | None:
+    """The wait word a call of `op` left in its workspace `ws` (None if the op has none); the
+    caller synchronises first."""
+    off = msa.msa_workspace_wait_word(op, dp.problem)
+    if off is None:
+        return None
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
 def sparse_attention_blocks(dp: DeviceProblem, ids, out=None, lse=None, ws=None, stream=None):
     """The prefill sparse branch on the block-centric schedule (same result as sparse_attention)."""
     if out is None:

@@ -111,6 +111,10 @@ def load():
     lib.msa_ceiling_mfma_bf16.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [ctypes.c_int, prob]
     lib.msa_workspace_size.restype = S
+    lib.msa_workspace_wait_word.argtypes = [ctypes.c_int, prob]
+    lib.msa_workspace_wait_word.restype = S
+    lib.msa_validate_host.argtypes = [prob, P, P, P]
+    lib.msa_validate_host.restype = ctypes.c_int
     lib.msa_status_string.argtypes = [ctypes.c_int]
     lib.msa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -164,6 +168,22 @@ def msa_workspace_size(op: int, problem: msa_problem_t) -> int:
     if n == SIZE_MAX:
         raise MsaError(MSA_ERROR_NOT_SUPPORTED, "msa_workspace_size")
     return int(n)
+
+
+def msa_workspace_wait_word(op: int, problem: msa_problem_t):
+    """Byte offset of the call's wait word in its workspace, or None if the op has none."""
+    n = load().msa_workspace_wait_word(int(op), ctypes.byref(problem))
+    return None if n == SIZE_MAX else int(n)
+
+
+def msa_validate_host(problem: msa_problem_t, cu_seqlens_q, cu_seqlens_k, topk_ids=None) -> int:
+    """Run the library's host-side contract check on host (numpy) copies; returns the status."""
+    import numpy as np
+    cq = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    ck = np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
+    ids = None if topk_ids is None else np.ascontiguousarray(topk_ids, dtype=np.int32)
+    return int(load().msa_validate_host(ctypes.byref(problem), cq.ctypes.data, ck.ctypes.data,
+                                        None if ids is None else ids.ctypes.data))
 
 
 def _check(status, what):

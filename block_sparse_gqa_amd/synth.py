@@ -63,7 +63,8 @@ class Workload:
 
     @property
     def is_decode(self) -> bool:
-        return max(self.seqlens_q) == 1
+        """Exactly one query per sequence (the decode entry points' shape)."""
+        return min(self.seqlens_q) == 1 and max(self.seqlens_q) == 1
 
     @property
     def total_q(self) -> int:

@@ -17,8 +17,10 @@
  *    H = num_heads, h = num_kv_heads (= GQA groups = index queries per token),
  *    d = head_dim, d_idx = index_dim.  Query head q belongs to group q / (H/h).
  *  - cu_seqlens_q / cu_seqlens_k are DEVICE int32 arrays of num_seqs+1
- *    non-decreasing offsets into the packed tensors, with
- *    len_k(s) >= len_q(s) >= 1 for every sequence.
+ *    non-decreasing offsets into the packed tensors, starting at 0 and
+ *    ending at total_q / total_k, with len_k(s) >= len_q(s) >= 0 for every
+ *    sequence: a sequence may have no queries (it is skipped), and
+ *    max_seqlen_q / max_seqlen_k must be at least the largest lengths.
  *  - Positions are bottom-right aligned: query row r of sequence s sits at
  *    p = len_k(s) - len_q(s) + r and sees keys 0..p of its own sequence.
  *    Prefill has len_q = len_k; decode has len_q = 1 (the query sees the
@@ -34,7 +36,13 @@
  *  - Errors: host-checkable argument problems return a non-zero status
  *    before anything is enqueued.  A failed launch returns
  *    MSA_ERROR_LAUNCH.  Device-side contents (cu_seqlens, topk_ids) are the
- *    caller's contract and are not checked.  No C++ exception crosses the ABI.
+ *    caller's contract and are not checked, except in the debug mode: with
+ *    the environment variable MSA_DEBUG_VALIDATE set (to anything but "" or
+ *    "0"), every entry point that reads them first copies cu_seqlens_q,
+ *    cu_seqlens_k and the ids it consumes to the host on `stream`, waits for
+ *    the copies (the one case where a call synchronises) and checks them with
+ *    msa_validate_host, returning MSA_ERROR_INVALID_VALUE before any launch
+ *    if they break the contract.  No C++ exception crosses the ABI.
  *  - Supported shapes: d in {64, 128}; d_idx in {32, 64}; B in {64, 128};
  *    1 <= H/h <= 16; h <= 64; 1 <= top_k <= 4096.
  */
@@ -102,7 +110,9 @@ typedef struct {
  *          ids of each row and group in ascending order, -1 in unused slots.
  * workspace: device scratch of at least msa_workspace_size(MSA_OP_INDEX_TOPK)
  *          bytes (block-level scores); NULL allowed only when that size is 0.
- * max_seqlen_q == 1 takes the decode variant (one query per sequence).
+ * max_seqlen_q == 1 with total_q == num_seqs (one query per sequence) takes
+ * the decode variant, a bandwidth-bound scan; any other batch, empty
+ * sequences included, takes the prefill variant.
  */
 msa_status_t msa_index_topk(const msa_problem_t *problem, const msa_bf16_t *q_idx,
                             const msa_bf16_t *k_idx, int32_t *topk_ids, void *workspace,
@@ -151,7 +161,11 @@ msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf1
  * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_PREFILL_TILES)
  * bytes, 16-byte aligned: an fp16 copy of v (every value scaled by one power
  * of two that puts max |v| in [2^14, 2^15), undone on the output) used for
- * the P.V products, plus a few KB.
+ * the P.V products, plus a few KB, among them the wait word (see
+ * msa_workspace_wait_word): the waves of a workgroup hand staged K/V
+ * sub-blocks to one another through LDS, and each hand-off wait is bounded;
+ * a wait that reaches its bound is counted there and the output of that
+ * call is then not valid.
  */
 msa_status_t msa_sparse_attn_prefill_tiles(const msa_problem_t *problem, const msa_bf16_t *q,
                                            const msa_bf16_t *k, const msa_bf16_t *v, const int32_t *topk_ids,
@@ -341,6 +355,32 @@ msa_status_t msa_ceiling_mfma_bf16(int32_t iterations, float *sink, double *flop
 /* Workspace bytes an entry point needs for `problem` (0 if none).  Returns
  * (size_t)-1 when the problem is invalid or unsupported for that op. */
 size_t msa_workspace_size(int op, const msa_problem_t *problem);
+
+/* Byte offset, inside the workspace of `op` for `problem`, of a uint32 word
+ * (4-byte aligned) that the call clears and then sets to the number of
+ * bounded waits that gave up: 0 after a call means every wait ended
+ * normally; anything else means that call's output is not valid.  The word
+ * is written on the call's stream, so read it after the call has completed.
+ * Ops whose kernels never wait on one another (and the prefill call when it
+ * picks the block-centric schedule) have no such word: (size_t)-1, as for
+ * an invalid or unsupported problem.  The environment variable
+ * MSA_DEBUG_SPIN_LIMIT (a non-negative integer, read at each call) lowers
+ * the bound, so that a test can make the waits give up while every kernel
+ * still ends normally. */
+size_t msa_workspace_wait_word(int op, const msa_problem_t *problem);
+
+/* Host-side check of the contract on device-resident inputs, run on host
+ * copies: cu_seqlens_q / cu_seqlens_k [num_seqs + 1] start at 0, end at
+ * total_q / total_k, give 0 <= len_q <= len_k per sequence and lengths no
+ * larger than max_seqlen_q / max_seqlen_k; and, when topk_ids [total_q, h,
+ * top_k] is not NULL, every id is -1 or an eligible block (0 <= j <=
+ * p / block_size for the row's position p) and no (row, group) holds an id
+ * twice.  Only the problem's host fields are read (its device pointers are
+ * ignored).  Returns MSA_SUCCESS or MSA_ERROR_INVALID_VALUE; touches no GPU
+ * and needs none.  The debug mode (MSA_DEBUG_VALIDATE) runs it inside the
+ * entry points. */
+msa_status_t msa_validate_host(const msa_problem_t *problem, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_k, const int32_t *topk_ids);
 
 /* Static, human-readable text of a status code. */
 const char *msa_status_string(msa_status_t status);

@@ -27,6 +27,43 @@ def check_selection_invariants(ids, E, k):
     assert (np.diff(sel) > 0).all(), ids
 
 
+def selection_report(oracle, inp, rows, gpu_ids, ref_ids, kth, tie):
+    """The same rule as compare_ids, counted instead of asserted: rows, (row, group) pairs, near ties,
+    in-band flips (pairs that differ only inside the near-tie band), and exact mismatches (pairs that
+    differ outside it, or break the selection invariants)."""
+    wl = inp.wl
+    B, k, h = wl.block_size, wl.top_k, wl.num_kv_heads
+    report = dict(rows=len(rows), pairs=len(rows) * h, near_tie=int(tie.sum()), exact_mismatch=0,
+                  band_flips=0)
+    seq_of = np.searchsorted(inp.cu_seqlens_q, rows, side="right") - 1
+    for i, row in enumerate(rows):
+        s = seq_of[i]
+        lq = inp.cu_seqlens_q[s + 1] - inp.cu_seqlens_q[s]
+        lk = inp.cu_seqlens_k[s + 1] - inp.cu_seqlens_k[s]
+        E = (lk - lq + (row - inp.cu_seqlens_q[s])) // B + 1
+        for g in range(h):
+            gi, ri = gpu_ids[i, g], ref_ids[i, g]
+            try:
+                check_selection_invariants(gi, E, k)
+            except AssertionError:
+                report["exact_mismatch"] += 1
+                continue
+            if np.array_equal(gi, ri):
+                continue
+            if not tie[i, g]:
+                report["exact_mismatch"] += 1
+                continue
+            S = oracle.block_scores(inp, int(row), g)
+            a, b = float(kth[i, g, 0]), float(kth[i, g, 1])
+            tol = BAND * max(abs(a), abs(b))
+            diff = set(gi[gi >= 0].tolist()) ^ set(ri[ri >= 0].tolist())
+            if all(abs(float(S[j]) - a) <= tol for j in diff):
+                report["band_flips"] += 1
+            else:
+                report["exact_mismatch"] += 1
+    return report
+
+
 def compare_ids(oracle, inp, rows, gpu_ids, ref_ids, kth, tie):
     """Returns a report dict; raises AssertionError on a violation."""
     wl = inp.wl

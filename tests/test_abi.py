@@ -266,3 +266,75 @@ def test_block_prefill_rejects(lib):
     assert attn_call(lib, blk, prob(), ws=None) == msa.MSA_ERROR_WORKSPACE
     assert attn_call(lib, blk, prob(), ws=FAKE, ws_bytes=need - 1) == msa.MSA_ERROR_WORKSPACE
     assert attn_call(lib, blk, prob(total_q=0, max_seqlen_q=0), q=None) == msa.MSA_SUCCESS
+
+
+def test_wait_word_offsets(lib):
+    p = prob()
+    # the tile schedule's workspace ends in a 256-byte slot: scale exponent, then the wait word
+    need = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
+    off = msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, p)
+    assert off == need - 256 + 4 and off % 4 == 0
+    # the automatic call on the tiles has the same word; on the block-centric schedule it has none
+    assert msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL, p) == off
+    long_ctx = prob(total_q=131072, total_k=131072, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,
+                    num_kv_heads=8, block_size=128, top_k=16)
+    assert msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL, long_ctx) is None
+    for op in (msa.MSA_OP_INDEX_TOPK, msa.MSA_OP_SPARSE_ATTN_DECODE, msa.MSA_OP_SPARSE_ATTN_BACKWARD,
+               msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, 99):
+        assert msa.msa_workspace_wait_word(op, p) is None
+    assert msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, prob(head_dim=96)) is None
+
+
+def host_prob(lens_q, lens_k, k=2, h=2, B=64):
+    return prob(num_seqs=len(lens_q), total_q=sum(lens_q), total_k=sum(lens_k), max_seqlen_q=max(lens_q),
+                max_seqlen_k=max(lens_k), num_kv_heads=h, num_heads=2 * h, block_size=B, top_k=k)
+
+
+def cu(lens):
+    import numpy as np
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def test_validate_host_seqlens(lib):
+    ok = msa.MSA_SUCCESS
+    bad = msa.MSA_ERROR_INVALID_VALUE
+    lq, lk = [3, 0, 2], [130, 5, 2]
+    p = host_prob(lq, lk)
+    assert msa.msa_validate_host(p, cu(lq), cu(lk)) == ok            # an empty sequence is allowed
+    assert msa.msa_validate_host(p, cu(lq) + 1, cu(lk)) == bad       # must start at 0
+    assert msa.msa_validate_host(p, cu(lq), cu([130, 5, 3])) == bad  # must end at total_k
+    assert msa.msa_validate_host(p, cu(lq), cu([130, 6, 1])) == bad  # len_k 1 < len_q 2 in the last sequence
+    p_small = host_prob(lq, lk)
+    p_small.max_seqlen_k = 100                                       # a sequence longer than max_seqlen_k
+    assert msa.msa_validate_host(p_small, cu(lq), cu(lk)) == bad
+    p_q = host_prob(lq, lk)
+    p_q.max_seqlen_q = 2
+    assert msa.msa_validate_host(p_q, cu(lq), cu(lk)) == bad
+    # decreasing offsets
+    assert msa.msa_validate_host(host_prob([2, 2], [4, 4]), [0, 2, 4], [0, 4, 8]) == ok
+    assert msa.msa_validate_host(host_prob([2, 2], [4, 4]), [0, 5, 4], [0, 4, 8]) == bad
+    # len_q > len_k
+    assert msa.msa_validate_host(host_prob([2, 2], [4, 4]), [0, 2, 4], [0, 1, 8]) == bad
+
+
+def test_validate_host_ids(lib):
+    import numpy as np
+    ok, bad = msa.MSA_SUCCESS, msa.MSA_ERROR_INVALID_VALUE
+    lq, lk = [3, 2], [130, 2]          # positions 127..129 (E = 2, 3, 3) and 0, 1 (E = 1)
+    p = host_prob(lq, lk, k=2, h=2)
+    ids = np.full((5, 2, 2), -1, np.int32)
+    ids[:, :, 0] = 0
+    ids[1:3, 1, 1] = 2
+    assert msa.msa_validate_host(p, cu(lq), cu(lk), ids) == ok
+    for r, g, a, j in ((0, 0, 1, 2),    # block 2 is not eligible at position 127
+                       (3, 1, 1, 1),    # nor block 1 at position 0
+                       (2, 0, 1, 0),    # a duplicate in one (row, group)
+                       (4, 0, 0, -2)):  # ids below -1
+        bad_ids = ids.copy()
+        bad_ids[r, g, a] = j
+        assert msa.msa_validate_host(p, cu(lq), cu(lk), bad_ids) == bad, (r, g, a, j)
+    # the same block in two groups of one row is fine
+    ids2 = ids.copy()
+    ids2[0, 1, 1] = 1
+    ids2[0, 0, 1] = 1
+    assert msa.msa_validate_host(p, cu(lq), cu(lk), ids2) == ok

@@ -45,11 +45,18 @@ def run_gpu(inp, ids_override=None):
         res["lse_given"] = lse2.cpu().numpy()
         if not inp.wl.is_decode:
             # both prefill schedules explicitly, whichever the call above chose
-            for name, fn in (("tiles", device.sparse_attention_tiles), ("blocks", device.sparse_attention_blocks)):
-                o3, l3 = fn(dp, ids2)
+            from block_sparse_gqa_amd import msa
+            for name, fn, op in (("tiles", device.sparse_attention_tiles, msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES),
+                                 ("blocks", device.sparse_attention_blocks, msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS)):
+                ws = device.workspace(dp, op)
+                o3, l3 = fn(dp, ids2, ws=ws)
+                torch.cuda.synchronize()
+                if name == "tiles":
+                    # every hand-off wait between the waves ended before its bound
+                    assert device.wait_word(dp, op, ws) == 0
                 res[f"out_{name}"] = o3.float().cpu().numpy()
                 res[f"lse_{name}"] = l3.cpu().numpy()
-                del o3, l3
+                del o3, l3, ws
                 torch.cuda.empty_cache()
     torch.cuda.synchronize()
     del dp
@@ -99,6 +106,9 @@ SMALL = [
     ("decode_k_over_E", (1, 1), (200, 3000), 16, 4, 128, 64, 64, 64, False),
     ("chunked_prefill", (100, 37), (300, 400), 8, 4, 128, 64, 64, 3, False),
     ("empty_sequences", (0, 300, 0, 129), (0, 300, 0, 129), 8, 2, 128, 64, 64, 3, True),
+    # one query per non-empty sequence, with empty ones before and between: not the decode shape
+    # (total_q != num_seqs), so the index call takes the prefill kernel, which skips them
+    ("decode_like_empty_seqs", (0, 1, 0, 1), (50, 700, 300, 1500), 32, 8, 128, 64, 64, 8, False),
 ]
 
 
