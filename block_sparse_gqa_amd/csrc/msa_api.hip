@@ -295,6 +295,28 @@ msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+msa_status_t msa_sparse_attn_decode_noalloc(const msa_problem_t *problem, const msa_bf16_t *q,
+                                            const msa_bf16_t *k_cache, const msa_bf16_t *v_cache,
+                                            const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out,
+                                            float *lse, msa_stream_t stream) {
+    msa_status_t st = check_problem(problem);
+    if (st != MSA_SUCCESS) return st;
+    const msa_problem_t &p = *problem;
+    if (p.total_q == 0) return MSA_SUCCESS;
+    if (p.max_seqlen_q != 1 || p.total_q != p.num_seqs) return MSA_ERROR_INVALID_VALUE;
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || topk_ids == nullptr || out == nullptr)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
+    if ((st = attn_support(p)) != MSA_SUCCESS) return st;
+    const Shape s = to_shape(p);
+    if (msa::decode_workspace_bytes(s) > msa::decode_scratch_bytes()) return MSA_ERROR_WORKSPACE;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (debug_validate_on() && (st = debug_validate(p, topk_ids, hs)) != MSA_SUCCESS) return st;
+    void *scratch = nullptr;
+    if (msa::decode_scratch(&scratch) != hipSuccess) return MSA_ERROR_LAUNCH;
+    return launched(msa::launch_attn_decode(s, q, k_cache, v_cache, topk_ids, softmax_scale, out, lse, scratch, hs));
+}
+
 namespace {
 
 // The paged entry points: decode only, a table and a pool of at least one page.

@@ -81,6 +81,10 @@ hipError_t launch_attn_backward(const Shape &s, const uint16_t *q, const uint16_
                                 hipStream_t st);
 int decode_splits(const Shape &s);
 size_t decode_workspace_bytes(const Shape &s);
+// The library's fixed decode scratch (allocation-free entry point): its size,
+// and its device address on the current device.
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void **ptr);
 hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                               hipStream_t st);

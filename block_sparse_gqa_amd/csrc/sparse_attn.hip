@@ -18,8 +18,19 @@
 //                   ds_read_b64_tr_b16.
 // Decode splits a sequence's selected blocks over many waves and merges the
 // partial results by log-sum-exp.
+#include <mutex>
+
+#include "msa.h"
 #include "msa_device.h"
 #include "msa_internal.h"
+
+// Fixed device memory for the allocation-free decode entry point: its split
+// partials (the workspace msa_sparse_attn_decode takes from the caller).  Each
+// GPU the library runs on holds its own copy from module load until the
+// process ends.  Host code never uses this name as an address: the per-device
+// address comes from hipGetSymbolAddress below.
+constexpr size_t kDecodeScratchBytes = MSA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
 
 namespace msa {
 
@@ -401,6 +412,30 @@ hipError_t launch_attn_decode(const Shape &s, const uint16_t *q, const uint16_t 
     if (s.d == 128 && s.B == 64) return launch_decode<128, 64>(s, q, k, v, ids, scale, out, lse, ws, st);
     if (s.d == 128 && s.B == 128) return launch_decode<128, 128>(s, q, k, v, ids, scale, out, lse, ws, st);
     return hipErrorInvalidValue;
+}
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+hipError_t decode_scratch(void **ptr) {
+    // Device address of `scratch` on the current device, looked up once per
+    // device (with that device current) and kept.
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace msa

@@ -93,6 +93,8 @@ def load():
     lib.msa_sparse_attn_prefill_blocks.restype = ctypes.c_int
     lib.msa_sparse_attn_decode.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P, S, P]
     lib.msa_sparse_attn_decode.restype = ctypes.c_int
+    lib.msa_sparse_attn_decode_noalloc.argtypes = [prob, P, P, P, P, ctypes.c_float, P, P, P]
+    lib.msa_sparse_attn_decode_noalloc.restype = ctypes.c_int
     paged = ctypes.POINTER(msa_paged_kv_t)
     lib.msa_index_topk_paged.argtypes = [prob, paged, P, P, P, P, S, P]
     lib.msa_index_topk_paged.restype = ctypes.c_int
@@ -229,6 +231,17 @@ def msa_sparse_attn_decode(problem, q, k_cache, v_cache, topk_ids, softmax_scale
                                          _ptr(topk_ids), float(softmax_scale), _ptr(out), _ptr(lse),
                                          _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "msa_sparse_attn_decode")
+
+
+MSA_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def msa_sparse_attn_decode_noalloc(problem, q, k_cache, v_cache, topk_ids, softmax_scale, out, lse=None,
+                                   stream=None):
+    """msa_sparse_attn_decode with the library's fixed scratch instead of a workspace."""
+    _check(load().msa_sparse_attn_decode_noalloc(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                 _ptr(topk_ids), float(softmax_scale), _ptr(out), _ptr(lse),
+                                                 _stream(stream)), "msa_sparse_attn_decode_noalloc")
 
 
 def make_paged(block_table, num_pages) -> msa_paged_kv_t:

@@ -191,6 +191,30 @@ msa_status_t msa_sparse_attn_decode(const msa_problem_t *problem, const msa_bf16
                                     msa_stream_t stream);
 
 /*
+ * msa_sparse_attn_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same problem, arguments, layouts,
+ * result and errors as msa_sparse_attn_decode (the same kernels run), except
+ * that the split partials live in a fixed device array inside the library:
+ * MSA_DECODE_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load
+ * until the process ends.  A problem whose
+ * msa_workspace_size(MSA_OP_SPARSE_ATTN_DECODE) exceeds that returns
+ * MSA_ERROR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing and frees nothing; its first call on a GPU looks the array's
+ * address up on that GPU (the current device) once.  Every call on one GPU
+ * shares that GPU's array, which keeps the last call's partials (nothing in
+ * it needs clearing: each split writes its partial before the merge reads
+ * it): calls that overlap in time on one GPU -- on different streams, or
+ * from threads without an order between them -- race and give wrong
+ * results; calls ordered on one stream do not.
+ */
+#define MSA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+msa_status_t msa_sparse_attn_decode_noalloc(const msa_problem_t *problem, const msa_bf16_t *q,
+                                            const msa_bf16_t *k_cache, const msa_bf16_t *v_cache,
+                                            const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out,
+                                            float *lse, msa_stream_t stream);
+
+/*
  * msa_sparse_attn_prefill on the block-centric ("KV-outer, gather-Q")
  * schedule: the same result, computed key block by key block.  The pages
  * name this operator flow ("深度解析M3多模态模型与Token Plan", section 二.2)
