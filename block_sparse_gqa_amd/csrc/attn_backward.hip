@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
     __shared__ __attribute__((aligned(16))) char vt[B * kRowStride];
     __shared__ __attribute__((aligned(16))) char qc[kRows * kRowStride];
     __shared__ __attribute__((aligned(16))) char doc[kRows * kRowStride];
-    __shared__ __attribute__((aligned(16))) char dst[kRows * DS_STRIDE];
+    __shared__ __attribute__((aligned(16))) char dst[kRows * DS_STRIDE];      // dS, bf16 head
+    __shared__ __attribute__((aligned(16))) char dst_lo[kRows * DS_STRIDE];   // dS, bf16 tail
     // per-row data of the current and the next chunk
     __shared__ int r_row[2][kRows], r_slot[2][kRows], r_pos[2][kRows];
     __shared__ float r_lse2[2][kRows], r_delta[2][kRows];
@@ -249,24 +250,39 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
                     pv[mt][i] = p;
                     dsv[mt][i] = p * (pa[mt][i] - dlt[mt][i]);
                 }
-            // A operands: k slot 8*q4 + i <- row 4*q4 + i (i < 4), row 16 + 4*q4 + i - 4
-            const bf16x8 pA = as_bf16x8(uint4{pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
-                                              pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])});
-            const bf16x8 dsA = as_bf16x8(uint4{pack_bf16x2(dsv[0][0], dsv[0][1]), pack_bf16x2(dsv[0][2], dsv[0][3]),
-                                               pack_bf16x2(dsv[1][0], dsv[1][1]), pack_bf16x2(dsv[1][2], dsv[1][3])});
+            // A operands: k slot 8*q4 + i <- row 4*q4 + i (i < 4), row 16 + 4*q4 + i - 4.
+            // P and dS enter the products as a bf16 head plus a bf16 tail
+            // (x = head + tail to 2^-17 |x|), so their rounding stays far
+            // below that of the bf16 outputs; dO, Q and K are bf16 inputs and
+            // exact as they are.
+            uint32_t pl[4], dl[4];
+            const uint32_t ph[4] = {split_bf16x2(pv[0][0], pv[0][1], &pl[0]), split_bf16x2(pv[0][2], pv[0][3], &pl[1]),
+                                    split_bf16x2(pv[1][0], pv[1][1], &pl[2]), split_bf16x2(pv[1][2], pv[1][3], &pl[3])};
+            const uint32_t dh[4] = {split_bf16x2(dsv[0][0], dsv[0][1], &dl[0]),
+                                    split_bf16x2(dsv[0][2], dsv[0][3], &dl[1]),
+                                    split_bf16x2(dsv[1][0], dsv[1][1], &dl[2]),
+                                    split_bf16x2(dsv[1][2], dsv[1][3], &dl[3])};
+            const bf16x8 pA = as_bf16x8(uint4{ph[0], ph[1], ph[2], ph[3]});
+            const bf16x8 pAl = as_bf16x8(uint4{pl[0], pl[1], pl[2], pl[3]});
+            const bf16x8 dsA = as_bf16x8(uint4{dh[0], dh[1], dh[2], dh[3]});
+            const bf16x8 dsAl = as_bf16x8(uint4{dl[0], dl[1], dl[2], dl[3]});
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                dva[u][dt] = mfma16x16x32(pA, tr_rows(doc, 0, dt), dva[u][dt]);
-                dka[u][dt] = mfma16x16x32(dsA, tr_rows(qc, 0, dt), dka[u][dt]);
+                const bf16x8 dob = tr_rows(doc, 0, dt), qb = tr_rows(qc, 0, dt);
+                dva[u][dt] = mfma16x16x32(pA, dob, dva[u][dt]);
+                dka[u][dt] = mfma16x16x32(dsA, qb, dka[u][dt]);
+                dva[u][dt] = mfma16x16x32(pAl, dob, dva[u][dt]);
+                dka[u][dt] = mfma16x16x32(dsAl, qb, dka[u][dt]);
             }
-            // dS to LDS, [row][token], for the dq products
+            // dS (head and tail) to LDS, [row][token], for the dq products
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t b = pack_bf16x2(dsv[mt][i], 0.f);
-                    *reinterpret_cast<uint16_t *>(dst + (16 * mt + 4 * q4 + i) * DS_STRIDE + 2 * (16 * tt + l16)) =
-                        (uint16_t)(b & 0xffffu);
+                    const int at = (16 * mt + 4 * q4 + i) * DS_STRIDE + 2 * (16 * tt + l16);
+                    const uint32_t w = dh[2 * mt + (i >> 1)], wl = dl[2 * mt + (i >> 1)];
+                    *reinterpret_cast<uint16_t *>(dst + at) = (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu));
+                    *reinterpret_cast<uint16_t *>(dst_lo + at) = (uint16_t)((i & 1) ? (wl >> 16) : (wl & 0xffffu));
                 }
         }
         __syncthreads();
@@ -278,10 +294,13 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
 #pragma unroll
             for (int s32 = 0; s32 < B / 32; ++s32) {
                 const bf16x8 a = tr_rows(kt, 32 * s32, dt);
-                const char *pr = dst + (16 * mt + l16) * DS_STRIDE + 2 * (32 * s32 + 4 * q4);
-                const uint2 lo2 = *reinterpret_cast<const uint2 *>(pr);
-                const uint2 hi2 = *reinterpret_cast<const uint2 *>(pr + 32);
+                const int at = (16 * mt + l16) * DS_STRIDE + 2 * (32 * s32 + 4 * q4);
+                const uint2 lo2 = *reinterpret_cast<const uint2 *>(dst + at);
+                const uint2 hi2 = *reinterpret_cast<const uint2 *>(dst + at + 32);
+                const uint2 lo2t = *reinterpret_cast<const uint2 *>(dst_lo + at);
+                const uint2 hi2t = *reinterpret_cast<const uint2 *>(dst_lo + at + 32);
                 acc = mfma16x16x32(a, as_bf16x8(uint4{lo2.x, lo2.y, hi2.x, hi2.y}), acc);
+                acc = mfma16x16x32(a, as_bf16x8(uint4{lo2t.x, lo2t.y, hi2t.x, hi2t.y}), acc);
             }
             const int r = 16 * mt + l16;
             const int row = r_row[cur][r];

@@ -52,7 +52,7 @@ def _load():
                                                     ctypes.c_float, i64, P, P, P, i32]
         lib.msa_oracle_sparse_attention.restype = i32
         lib.msa_oracle_sparse_attention_backward.argtypes = [i32, P, P, i32, i32, i32, i32, i32, P, P, P, P,
-                                                             ctypes.c_float, P, P, P, P, i32]
+                                                             ctypes.c_float, P, P, P, P, P, i32]
         lib.msa_oracle_sparse_attention_backward.restype = i32
         _lib = lib
     return _lib
@@ -137,9 +137,12 @@ def sparse_attention(inp, ids, rows=None, scale=None, threads: int = 0):
     return out, lse
 
 
-def sparse_attention_backward(inp, ids, dout, scale=None, threads: int = 0):
+def sparse_attention_backward(inp, ids, dout, scale=None, threads: int = 0, out=None):
     """Oracle backward of the sparse branch with the selection ``ids``
     [total_q, h, k] held fixed; ``dout`` [total_q, H, d] holds bf16 bits.
+    ``out`` (optional, [total_q, H, d] bf16 bits): the forward output the
+    backward is handed, used for D = dO . out; without it D = sum_t P_t dP_t,
+    i.e. dO . O with the exact output.
     Returns (dq [total_q, H, d], dk [total_k, h, d], dv [total_k, h, d]) float32."""
     wl = inp.wl
     ids = _c(ids, np.int32)
@@ -152,10 +155,13 @@ def sparse_attention_backward(inp, ids, dout, scale=None, threads: int = 0):
     dv = np.empty((tk, h, d), np.float32)
     cu_q, cu_k = _c(inp.cu_seqlens_q, np.int32), _c(inp.cu_seqlens_k, np.int32)
     q, kk, v, do = (_c(x, np.uint16) for x in (inp.q, inp.k, inp.v, dout))
+    ob = None if out is None else _c(out, np.uint16)
+    if ob is not None and ob.shape != do.shape:
+        raise ValueError("out must be [total_q, H, d] like dout")
     sc = wl.scale if scale is None else scale
     rc = _load().msa_oracle_sparse_attention_backward(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), H, h, d,
                                                       wl.block_size, ids.shape[2], _ptr(q), _ptr(kk), _ptr(v),
-                                                      _ptr(ids), ctypes.c_float(sc), _ptr(do), _ptr(dq), _ptr(dk),
+                                                      _ptr(ids), ctypes.c_float(sc), _ptr(do), _ptr(ob), _ptr(dq), _ptr(dk),
                                                       _ptr(dv), threads)
     if rc != 0:
         raise ValueError("oracle sparse_attention_backward rejected its input")

@@ -354,6 +354,7 @@ int msa_oracle_sparse_attention_backward(int num_seqs, const int32_t *cu_q, cons
                                          int H, int h, int d, int B, int top_k,
                                          const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                          const int32_t *ids, float scale, const uint16_t *dout,
+                                         const uint16_t *out,
                                          float *dq, float *dk, float *dv, int nthreads)
 {
     if (num_seqs < 1 || h < 1 || H < h || H % h || d < 1 || B < 1 || top_k < 1) return -1;
@@ -406,7 +407,9 @@ int msa_oracle_sparse_attention_backward(int num_seqs, const int32_t *cu_q, cons
                     Z += P[a];
                 }
                 for (int64_t a = 0; a < n; ++a) P[a] /= Z;
-                /* dP_t = dO . v_t and D = sum_t P_t dP_t */
+                /* dP_t = dO . v_t and D = sum_t P_t dP_t (= dO . O for the exact
+                 * output O); when the caller hands in the forward's output
+                 * `out` (bf16, as a backward receives it), D = dO . out */
                 float Dsum = 0.0f;
                 for (int64_t a = 0; a < n; ++a) {
                     const uint16_t *vt = v + (tok[a] * h + g) * (int64_t)d;
@@ -414,6 +417,11 @@ int msa_oracle_sparse_attention_backward(int num_seqs, const int32_t *cu_q, cons
                     for (int c = 0; c < d; ++c) s += bf16_to_float(dor[c]) * bf16_to_float(vt[c]);
                     dP[a] = s;
                     Dsum += P[a] * s;
+                }
+                if (out != NULL) {
+                    const uint16_t *orow = out + (row * H + head) * (int64_t)d;
+                    Dsum = 0.0f;
+                    for (int c = 0; c < d; ++c) Dsum += bf16_to_float(dor[c]) * bf16_to_float(orow[c]);
                 }
                 float *dqr = dq + (row * H + head) * (int64_t)d;
                 for (int64_t a = 0; a < n; ++a) {

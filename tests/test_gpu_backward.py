@@ -2,13 +2,18 @@
 dq, dk, dv from msa_sparse_attn_prefill_backward against the oracle's plain
 chain rule, on the GPU's own ids, out and lse.
 
-Tolerance.  The kernels take P and dS in bf16 for the dV, dK and dQ products
-(relative rounding 2^-9) and round dq, dk, dv to bf16; each output element is
-a sum of such terms with both signs, so its error is bounded by a small
-multiple of 2^-9 times the sum of the magnitudes of its terms, which is at
-most the tensor's largest magnitude times a few.  The check is
-|gpu - ref| <= 1e-2 |ref| + 1e-2 max|ref| per tensor, with the largest
-observed ratio printed for each case.
+The backward is handed the forward's output `out` in bf16 and forms
+D = dO . out from it, as its contract says; the oracle gets the same `out`
+(its given-output path, pinned to float64 autograd), so both compute the same
+function of the same inputs.
+
+Tolerance: the forward's, |gpu - ref| <= 2e-3 + 1e-2 |ref| per element.  The
+kernels take P and dS into the dV, dK and dQ products as a bf16 head plus a
+bf16 tail (relative rounding about 2^-17), keep dq per (row, selected slot)
+as a bf16 partial, accumulate in float32 and round dq, dk, dv to bf16
+(2^-9 relative), which the relative term covers.  The distance to the exact
+gradient (D from the unrounded output) is printed beside it: it adds the
+effect of out's bf16 rounding on D.
 """
 import sys
 import zlib
@@ -23,8 +28,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-RTOL = 1e-2
-ATOL_REL = 1e-2
+from tests import parity
 
 
 def say(*a):
@@ -33,15 +37,11 @@ def say(*a):
 
 
 def check_grad(got, ref, name):
+    """The forward's elementwise tolerance; returns the largest error over its bound."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    scale = np.abs(ref).max()
-    bound = RTOL * np.abs(ref) + ATOL_REL * scale
-    err = np.abs(got - ref)
-    bad = err > bound
-    assert not bad.any(), (f"{name}: {int(bad.sum())} elements off; worst at {np.unravel_index(np.argmax(err - bound), err.shape)}"
-                           f" err {err.max():.3g} vs max|ref| {scale:.3g}")
-    return float(err.max() / max(scale, 1e-30))
+    parity.assert_close(got, ref, name)
+    return float((np.abs(got - ref) / (parity.ATOL + parity.RTOL * np.abs(ref))).max())
 
 
 CASES = [
@@ -77,10 +77,14 @@ def test_backward_matches_oracle(case):
     dq, dk, dv = device.sparse_attention_backward(dp, ids, out, lse, dout)
     torch.cuda.synchronize()
     gids = ids.cpu().numpy()
-    rq, rk, rv = oracle.sparse_attention_backward(inp, gids, dout_bits)
-    e = [check_grad(t.float().cpu().numpy(), r, f"{name} {n}")
-         for t, r, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"))]
-    say(f"[{name}] max |err| / max |ref|: dq {e[0]:.3g}, dk {e[1]:.3g}, dv {e[2]:.3g}")
+    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    rq, rk, rv = oracle.sparse_attention_backward(inp, gids, dout_bits, out=out_bits)
+    got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+    e = [check_grad(g_, r, f"{name} {n}") for g_, r, n in zip(got, (rq, rk, rv), ("dq", "dk", "dv"))]
+    say(f"[{name}] largest |err| / (2e-3 + 1e-2 |ref|): dq {e[0]:.3g}, dk {e[1]:.3g}, dv {e[2]:.3g}")
+    exact = oracle.sparse_attention_backward(inp, gids, dout_bits)
+    x = [float(np.abs(g_ - r).max() / np.abs(r).max()) for g_, r in zip(got, exact)]
+    say(f"[{name}] against the exact gradient, max |err| / max |ref|: dq {x[0]:.3g}, dk {x[1]:.3g}, dv {x[2]:.3g}")
 
 
 @pytest.mark.timeout(300)

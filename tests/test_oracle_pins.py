@@ -431,9 +431,15 @@ def test_forced_blocks_invariants(oracle_lib):
 # masked softmax attention is the independent reference.
 
 
-def autograd_reference(inp, ids, dout_bits):
+def autograd_reference(inp, ids, dout_bits, out_bits=None):
     """dq, dk, dv of sum(O * dO) for attention restricted to the visible tokens
-    of each group's selected blocks, by float64 autograd (per sequence)."""
+    of each group's selected blocks, by float64 autograd (per sequence).
+
+    With ``out_bits`` (a given forward output, bf16 bits) the loss gains
+    sum_rows c * lse, where lse is the row's log-sum-exp of the scaled logits
+    and c = dO.O - dO.out is held constant.  Since d lse / d s_t = P_t, this
+    turns every dS_t = P_t (dP_t - dO.O) into P_t (dP_t - dO.out): the gradient
+    a backward computes when it forms D from the output it is given."""
     torch = pytest.importorskip("torch")
     wl = inp.wl
     H, h, d, B = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
@@ -462,6 +468,10 @@ def autograd_reference(inp, ids, dout_bits):
         p_ = torch.softmax(logits, dim=-1)
         o = torch.einsum("rht,thd->rhd", p_, vv)
         loss = loss + (o * dout[q0:q1]).sum()
+        if out_bits is not None:
+            given = torch.tensor(f64(out_bits[q0:q1]))
+            c = ((o.detach() - given) * dout[q0:q1]).sum(dim=-1)            # [lq, H]
+            loss = loss + (c * torch.logsumexp(logits, dim=-1)).sum()
     loss.backward()
     return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
 
@@ -485,6 +495,27 @@ def test_backward_equals_autograd(oracle_lib, case):
     rq, rk, rv = autograd_reference(inp, ids, dout)
     for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
         np.testing.assert_allclose(got, ref, rtol=2e-4, atol=2e-5 * np.abs(ref).max(), err_msg=name)
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_backward_with_given_output_equals_autograd(oracle_lib, case):
+    """The backward handed the forward's output rounded to bf16 (as a caller passes it) forms
+    D = dO.out from it; autograd of sum(O dO) + sum c lse with c = dO.(O - out) is the same
+    gradient.  The rounding must also change the result (the given output is really used)."""
+    sq, sk, H, h, d, di, B, K = case
+    inp = make(sq, sk, H, h, d, di, B, K, seed=17)
+    ids, _, _ = oracle_lib.index_topk(inp)
+    o, _ = oracle_lib.sparse_attention(inp, ids)
+    out_bits = synth.f32_to_bf16_bits(o.astype(np.float32))
+    rng = np.random.default_rng(6)
+    dout = synth.f32_to_bf16_bits(rng.standard_normal(inp.q.shape).astype(np.float32))
+    got = oracle_lib.sparse_attention_backward(inp, ids, dout, out=out_bits)
+    ref = autograd_reference(inp, ids, dout, out_bits=out_bits)
+    for g_, r_, name in zip(got, ref, ("dq", "dk", "dv")):
+        np.testing.assert_allclose(g_, r_, rtol=2e-4, atol=2e-5 * np.abs(r_).max(), err_msg=name)
+    exact = oracle_lib.sparse_attention_backward(inp, ids, dout)
+    assert not np.array_equal(exact[0], got[0])
+    np.testing.assert_array_equal(exact[2], got[2])    # dv does not involve D
 
 
 def test_backward_untouched_tokens_get_zero(oracle_lib):
