@@ -79,8 +79,13 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
     const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
     const int32_t *__restrict__ off, const int32_t *__restrict__ entries, int num_seqs, int H, int h, int nb_max,
-    int top_k, float scale, float c2, uint16_t *__restrict__ dq_part, uint16_t *__restrict__ dk,
-    uint16_t *__restrict__ dv) {
+    int top_k, int row0, float scale, float c2, uint16_t *__restrict__ dq_part, uint16_t *__restrict__ dk,
+    uint16_t *__restrict__ dv, float *__restrict__ dk_acc, float *__restrict__ dv_acc) {
+    // The list entries are (row - row0) * top_k + slot for the rows of one
+    // chunk, and dq_part holds that chunk's rows.  dk_acc / dv_acc (float32,
+    // [total_k, h, d]) are null for a problem run in one chunk, where dk and
+    // dv are written as bf16 directly; otherwise each chunk adds its share
+    // there (a workgroup owns its block's rows within a launch).
     constexpr int KS = D / 32;           // 32-wide k steps over d
     constexpr int DT = D / 16;           // 16-wide d tiles
     constexpr int TPW = B / 64;          // 16-token tiles per wave
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
         const int qi = tid / G, hd = tid % G;
         const bool ok = qi < min(qpc, e1 - c0) && tid < qpc * G;
         const int e = ok ? entries[c0 + qi] : 0;
-        i_row = ok ? e / top_k : -1;
+        i_row = ok ? row0 + e / top_k : -1;
         i_slot = e % top_k;
         i_pos = ok ? shift + (i_row - q_begin) : -1;
         const size_t ix = (size_t)max(i_row, 0) * H + g * G + hd;
@@ -305,8 +310,8 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
             const int r = 16 * mt + l16;
             const int row = r_row[cur][r];
             if (row >= 0) {
-                uint16_t *dstq =
-                    dq_part + (((size_t)row * top_k + r_slot[cur][r]) * H + g * G + r % G) * D + 16 * dt + 4 * q4;
+                uint16_t *dstq = dq_part + (((size_t)(row - row0) * top_k + r_slot[cur][r]) * H + g * G + r % G) * D +
+                                 16 * dt + 4 * q4;
                 *reinterpret_cast<uint2 *>(dstq) =
                     uint2{pack_bf16x2(acc[0] * scale, acc[1] * scale), pack_bf16x2(acc[2] * scale, acc[3] * scale)};
             }
@@ -329,8 +334,13 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const size_t idx = rowbase + 16 * dt + l16;
-                dk[idx] = (uint16_t)(pack_bf16x2(dka[u][dt][i] * scale, 0.f) & 0xffffu);
-                dv[idx] = (uint16_t)(pack_bf16x2(dva[u][dt][i], 0.f) & 0xffffu);
+                if (dk_acc != nullptr) {
+                    dk_acc[idx] += dka[u][dt][i] * scale;
+                    dv_acc[idx] += dva[u][dt][i];
+                } else {
+                    dk[idx] = (uint16_t)(pack_bf16x2(dka[u][dt][i] * scale, 0.f) & 0xffffu);
+                    dv[idx] = (uint16_t)(pack_bf16x2(dva[u][dt][i], 0.f) & 0xffffu);
+                }
             }
         }
     }
@@ -343,14 +353,17 @@ __global__ __launch_bounds__(256, B == 64 ? 2 : 1) void bwd_block(
 template <int D>
 __global__ __launch_bounds__(256) void bwd_finish(const uint16_t *__restrict__ dq_part, const int32_t *__restrict__ ids,
                                                   const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
-                                                  int num_seqs, long n_rows, int H, int h, int B, int top_k,
-                                                  uint16_t *__restrict__ dq) {
+                                                  int num_seqs, int row0, long n_rows, int H, int h, int B,
+                                                  int top_k, uint16_t *__restrict__ dq) {
+    // rows [row0, row0 + n_rows / H) of one chunk; dq_part holds those rows
     constexpr int CPR = D / 8;        // 16-byte chunks per row
     constexpr int NSO = 64 / CPR;     // slot lane groups
-    const long rh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (rh >= n_rows) return;
+    const long rh0 = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rh0 >= n_rows) return;
     const int lane = threadIdx.x & 63, c = lane % CPR, so = lane / CPR;
-    const int row = (int)(rh / H), head = (int)(rh % H), g = head / (H / h);
+    const int rr = (int)(rh0 / H), head = (int)(rh0 % H), g = head / (H / h);
+    const int row = row0 + rr;
+    const long rh = (long)row * H + head;
     const int s = seq_of_row(cu_q, num_seqs, row);
     const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
     const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
@@ -361,7 +374,7 @@ __global__ __launch_bounds__(256) void bwd_finish(const uint16_t *__restrict__ d
     for (int a = so; a < top_k; a += NSO) {
         const int j = sel[a];
         const bool ok = j >= 0 && j <= p / B;
-        const uint4 x = load16(dq_part + (((size_t)row * top_k + (ok ? a : 0)) * H + head) * D + 8 * c);
+        const uint4 x = load16(dq_part + (((size_t)rr * top_k + (ok ? a : 0)) * H + head) * D + 8 * c);
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -379,13 +392,29 @@ __global__ __launch_bounds__(256) void bwd_finish(const uint16_t *__restrict__ d
                   pack_bf16x2(acc[6], acc[7])};
 }
 
-// Workspace: the block lists, then delta and the dq partials.
+// float32 dk, dv -> bf16 (a problem run in several chunks).
+__global__ __launch_bounds__(256) void bwd_kv_out(const float *__restrict__ dk_acc, const float *__restrict__ dv_acc,
+                                                  long n, uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
+    for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 2; i < n; i += (long)gridDim.x * 512) {
+        const float2 a = *reinterpret_cast<const float2 *>(dk_acc + i);
+        const float2 b = *reinterpret_cast<const float2 *>(dv_acc + i);
+        *reinterpret_cast<uint32_t *>(dk + i) = pack_bf16x2(a.x, a.y);
+        *reinterpret_cast<uint32_t *>(dv + i) = pack_bf16x2(b.x, b.y);
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_f32(float *__restrict__ p, long n) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0.f;
+}
+
+// Workspace: the block lists of one chunk, delta of every row, the chunk's dq
+// partials, and (several chunks only) float32 dk and dv.
 struct BwdWs {
     BlockLists lists;
-    size_t delta, dq_part, bytes;
+    size_t delta, dq_part, dk_acc, dv_acc, bytes;
 };
 
-BwdWs bwd_ws(const Shape &s) {
+BwdWs bwd_ws(const Shape &s, bool acc) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     BwdWs w;
     w.lists = block_lists_layout(s);
@@ -393,46 +422,92 @@ BwdWs bwd_ws(const Shape &s) {
     w.delta = at;
     at += al((size_t)s.total_q * s.H * sizeof(float));
     w.dq_part = at;
-    at += al((size_t)s.total_q * s.top_k * s.H * s.d * sizeof(uint16_t));
+    at += al((size_t)s.rows * s.top_k * s.H * s.d * sizeof(uint16_t));
+    w.dk_acc = w.dv_acc = 0;
+    if (acc) {
+        const size_t kv = al((size_t)s.total_k * s.h * s.d * sizeof(float));
+        w.dk_acc = at;
+        at += kv;
+        w.dv_acc = at;
+        at += kv;
+    }
     w.bytes = at;
     return w;
+}
+
+// Rows per chunk: the whole problem if its workspace fits the cap, else as
+// many as fit next to the float32 dk / dv accumulators.
+int bwd_chunk_rows(const Shape &s) {
+    Shape one = s;
+    one.rows = 1;
+    const size_t per_row = (size_t)s.h * s.top_k * 8 + (size_t)s.top_k * s.H * s.d * 2;
+    Shape all = s;
+    all.rows = s.total_q;
+    if (bwd_ws(all, false).bytes <= workspace_cap()) return s.total_q;
+    return chunk_rows(s, bwd_ws(one, true).bytes - per_row, per_row);
 }
 
 template <int D, int B>
 hipError_t launch_bwd(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *ids,
                       float scale, const uint16_t *out, const float *lse, const uint16_t *dout, uint16_t *dq,
                       uint16_t *dk, uint16_t *dv, void *ws, hipStream_t st) {
-    const BwdWs w = bwd_ws(s);
+    const int per = bwd_chunk_rows(s);
+    const bool chunked = per < s.total_q;
+    Shape c0 = s;
+    c0.rows = per;
+    const BwdWs wl = bwd_ws(c0, chunked);   // the largest chunk: delta and the accumulators sit where it puts them
     char *base = static_cast<char *>(ws);
-    float *delta = reinterpret_cast<float *>(base + w.delta);
-    uint16_t *dq_part = reinterpret_cast<uint16_t *>(base + w.dq_part);
-    const int32_t *blk_off = reinterpret_cast<const int32_t *>(base + w.lists.blk_off);
-    const int32_t *off = reinterpret_cast<const int32_t *>(base + w.lists.off);
-    const int32_t *entries = reinterpret_cast<const int32_t *>(base + w.lists.entries);
-    const long rows = (long)s.total_q * s.H;
-    auto grid_of = [](long n, long per) { return dim3((unsigned)((n + per - 1) / per)); };
-
-    hipLaunchKernelGGL((bwd_prep<D>), grid_of(rows, 4), dim3(256), 0, st, out, dout, rows, delta);
-    const hipError_t e = launch_block_lists(s, ids, w.lists, base, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_block<D, B>), dim3((unsigned)w.lists.nb_max, s.h), dim3(256), 0, st, q, k, v, dout, lse,
-                       delta, s.cu_q, s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max,
-                       s.top_k, scale, scale * kLog2e, dq_part, dk, dv);
-    hipLaunchKernelGGL((bwd_finish<D>), grid_of(rows, 4), dim3(256), 0, st, dq_part, ids, s.cu_q, s.cu_k, s.num_seqs,
-                       rows, s.H, s.h, s.B, s.top_k, dq);
+    float *delta = reinterpret_cast<float *>(base + wl.delta);
+    uint16_t *dq_part = reinterpret_cast<uint16_t *>(base + wl.dq_part);
+    float *dk_acc = chunked ? reinterpret_cast<float *>(base + wl.dk_acc) : nullptr;
+    float *dv_acc = chunked ? reinterpret_cast<float *>(base + wl.dv_acc) : nullptr;
+    auto grid_of = [](long n, long per_wg) { return dim3((unsigned)((n + per_wg - 1) / per_wg)); };
+    const long rows_all = (long)s.total_q * s.H;
+    hipLaunchKernelGGL((bwd_prep<D>), grid_of(rows_all, 4), dim3(256), 0, st, out, dout, rows_all, delta);
+    const long kv = (long)s.total_k * s.h * s.d;
+    if (chunked) {
+        hipLaunchKernelGGL(fill_zero_f32, grid_of(std::min(kv, 1L << 22), 256), dim3(256), 0, st, dk_acc, kv);
+        hipLaunchKernelGGL(fill_zero_f32, grid_of(std::min(kv, 1L << 22), 256), dim3(256), 0, st, dv_acc, kv);
+    }
+    for (int r0 = 0; r0 < s.total_q; r0 += per) {
+        Shape c = s;
+        c.row0 = r0;
+        c.rows = std::min(per, s.total_q - r0);
+        // the chunk's lists sit at the start of the workspace (their size
+        // grows with the rows, so a short last chunk fits where the first did)
+        const BlockLists lists = block_lists_layout(c);
+        const int32_t *blk_off = reinterpret_cast<const int32_t *>(base + lists.blk_off);
+        const int32_t *off = reinterpret_cast<const int32_t *>(base + lists.off);
+        const int32_t *entries = reinterpret_cast<const int32_t *>(base + lists.entries);
+        const hipError_t e = launch_block_lists(c, ids, lists, base, st);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_block<D, B>), dim3((unsigned)lists.nb_max, s.h), dim3(256), 0, st, q, k, v, dout, lse,
+                           delta, s.cu_q, s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)lists.nb_max,
+                           s.top_k, c.row0, scale, scale * kLog2e, dq_part, dk, dv, dk_acc, dv_acc);
+        const long rows = (long)c.rows * s.H;
+        hipLaunchKernelGGL((bwd_finish<D>), grid_of(rows, 4), dim3(256), 0, st, dq_part, ids, s.cu_q, s.cu_k,
+                           s.num_seqs, c.row0, rows, s.H, s.h, s.B, s.top_k, dq);
+    }
+    if (chunked)
+        hipLaunchKernelGGL(bwd_kv_out, grid_of(std::min(kv / 2, 1L << 22), 256), dim3(256), 0, st, dk_acc, dv_acc, kv,
+                           dk, dv);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(const Shape &s) { return bwd_ws(s).bytes; }
+size_t backward_workspace_bytes(const Shape &s) {
+    const int per = bwd_chunk_rows(s);
+    Shape c = s;
+    c.rows = per;
+    return bwd_ws(c, per < s.total_q).bytes;
+}
 
 hipError_t launch_attn_backward(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const int32_t *ids, float scale, const uint16_t *out, const float *lse,
                                 const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv, void *ws,
                                 hipStream_t st) {
     if (s.H / s.h > kRows) return hipErrorInvalidValue;
-    if ((long)s.total_q * s.top_k > 0x7fffffffL) return hipErrorInvalidValue;   // entries are row * top_k + slot
     if (s.d == 64 && s.B == 64) return launch_bwd<64, 64>(s, q, k, v, ids, scale, out, lse, dout, dq, dk, dv, ws, st);
     if (s.d == 64 && s.B == 128) return launch_bwd<64, 128>(s, q, k, v, ids, scale, out, lse, dout, dq, dk, dv, ws, st);
     if (s.d == 128 && s.B == 64) return launch_bwd<128, 64>(s, q, k, v, ids, scale, out, lse, dout, dq, dk, dv, ws, st);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
     const int32_t *__restrict__ off, const int32_t *__restrict__ entries, int num_seqs, int H, int h, int nb_max,
-    int top_k, float c2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_w) {
+    int top_k, int row0, float c2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_w) {
     constexpr int KS = D / 32;            // 32-wide k steps over d
     constexpr int DT = D / 16;            // 16-wide d tiles
     constexpr int TT = B / 16;            // 16-token tiles of the block
@@ -128,12 +128,12 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
         hd[mt] = (16 * mt + l16) % G;
     }
     const int ntiles = (nq + qpt - 1) / qpt;
-    auto entry = [&](int t, int mt) {   // row * top_k + slot, or -1
+    auto entry = [&](int t, int mt) {   // (row - row0) * top_k + slot, or -1
         const int x = t * qpt + qi[mt];
         return (t < ntiles && 16 * mt + l16 < rows_used && x < nq) ? entries[e0 + x] : -1;
     };
     auto load_q = [&](uint4 (&qo)[KS], int ent, int hh) {   // row 0 stands in for unused lanes
-        const size_t base = ((size_t)(ent >= 0 ? ent / top_k : 0) * H + g * G + hh) * D + 8 * q4;
+        const size_t base = ((size_t)(ent >= 0 ? row0 + ent / top_k : 0) * H + g * G + hh) * D + 8 * q4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qo[ks] = load16(q + base + 32 * ks);
     };
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
         float mu[MT], lsum[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int row = ent_cur[mt] >= 0 ? ent_cur[mt] / top_k : -1;
+            const int row = ent_cur[mt] >= 0 ? row0 + ent_cur[mt] / top_k : -1;
             const int lim = row >= 0 ? shift + (row - q_begin) - j * B : -1;
             float mx = -INFINITY;
 #pragma unroll
@@ -266,20 +266,21 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ part_o, const float2 *__restrict__ part_w,
                                                  const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
-                                                 const int32_t *__restrict__ cu_k, int num_seqs, long n_pairs, int H,
-                                                 int h, int B, int top_k, uint16_t *__restrict__ out,
-                                                 float *__restrict__ lse) {
+                                                 const int32_t *__restrict__ cu_k, int num_seqs, int row0,
+                                                 long n_pairs, int H, int h, int B, int top_k,
+                                                 uint16_t *__restrict__ out, float *__restrict__ lse) {
     constexpr int CPR = D / 8;       // 16-byte chunks per partial row
     constexpr int HPP = 64 / CPR;    // heads per pass
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const long rg = (long)blockIdx.x * 4 + wave;
     if (rg >= n_pairs) return;
     const int lane = threadIdx.x & 63, c = lane % CPR, hs = lane / CPR;
-    const int row = (int)(rg / h), g = (int)(rg % h), G = H / h;
+    const int rr = (int)(rg / h), g = (int)(rg % h), G = H / h;   // rr: row within the chunk
+    const int row = row0 + rr;
     const int s = seq_of_row(cu_q, num_seqs, row);
     const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
     const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
-    const size_t base = (size_t)row * top_k;
+    const size_t base = (size_t)rr * top_k;   // the chunk's partials
 
     for (int h0 = 0; h0 < G; h0 += HPP) {
         const bool live = h0 + hs < G;
@@ -329,9 +330,9 @@ FwdWs fwd_ws(const Shape &s) {
     w.lists = block_lists_layout(s);
     size_t at = w.lists.bytes;
     w.part_o = at;
-    at += al((size_t)s.total_q * s.top_k * s.H * s.d * sizeof(uint16_t));
+    at += al((size_t)s.rows * s.top_k * s.H * s.d * sizeof(uint16_t));
     w.part_w = at;
-    at += al((size_t)s.total_q * s.top_k * s.H * sizeof(float2));
+    at += al((size_t)s.rows * s.top_k * s.H * sizeof(float2));
     w.bytes = at;
     return w;
 }
@@ -349,17 +350,31 @@ hipError_t launch_fwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
     const hipError_t e = launch_block_lists(s, ids, w.lists, base, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_block<D, B>), dim3((unsigned)w.lists.nb_max, s.h), dim3(64 * fwd_waves<B>()), 0, st, q, k, v, s.cu_q,
-                       s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max, s.top_k,
+                       s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max, s.top_k, s.row0,
                        scale * kLog2e, part_o, part_w);
-    const long pairs = (long)s.total_q * s.h;
+    const long pairs = (long)s.rows * s.h;
     hipLaunchKernelGGL((fwd_merge<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, part_o, part_w, ids, s.cu_q,
-                       s.cu_k, s.num_seqs, pairs, s.H, s.h, s.B, s.top_k, out, lse);
+                       s.cu_k, s.num_seqs, s.row0, pairs, s.H, s.h, s.B, s.top_k, out, lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t block_prefill_workspace_bytes(const Shape &s) { return fwd_ws(s).bytes; }
+// Rows per chunk of the block-centric schedule: the lists' per-key arrays are
+// fixed, the entries, places and partials grow with the rows.
+int block_prefill_chunk_rows(const Shape &s) {
+    Shape one = s;
+    one.rows = 1;
+    const size_t fixed = fwd_ws(one).bytes;
+    const size_t per_row = (size_t)s.h * s.top_k * 8 + (size_t)s.top_k * s.H * (2 * s.d + 8);
+    return chunk_rows(s, fixed, per_row);
+}
+
+size_t block_prefill_workspace_bytes(const Shape &s) {
+    Shape c = s;
+    c.rows = block_prefill_chunk_rows(s);
+    return fwd_ws(c).bytes;
+}
 
 // The query tiles stage the union of a tile's selections once per tile, so
 // they pay off while a staged block serves many of the tile's queries: about
@@ -376,7 +391,6 @@ size_t block_prefill_workspace_bytes(const Shape &s) { return fwd_ws(s).bytes; }
 bool prefill_prefers_blocks(const Shape &s) {
     const int G = s.H / s.h;
     if (G < 1 || G > 16 || s.max_q < 1) return false;
-    if ((long)s.total_q * s.top_k > 0x7fffffffL) return false;   // entries are row * top_k + slot
     const double e_k = (double)((s.max_k + s.B - 1) / s.B), e_q = (double)((s.max_q + s.B - 1) / s.B);
     const double e_avg = std::max(1.0, e_k - 0.5 * e_q);
     const double r = (double)prefill_tile_queries(s) * std::min((double)s.top_k, e_k) / e_avg;
@@ -387,12 +401,22 @@ hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const u
                                       const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                       hipStream_t st) {
     if (s.H / s.h > 16) return hipErrorInvalidValue;
-    if ((long)s.total_q * s.top_k > 0x7fffffffL) return hipErrorInvalidValue;   // entries are row * top_k + slot
-    if (s.d == 64 && s.B == 64) return launch_fwd<64, 64>(s, q, k, v, ids, scale, out, lse, ws, st);
-    if (s.d == 64 && s.B == 128) return launch_fwd<64, 128>(s, q, k, v, ids, scale, out, lse, ws, st);
-    if (s.d == 128 && s.B == 64) return launch_fwd<128, 64>(s, q, k, v, ids, scale, out, lse, ws, st);
-    if (s.d == 128 && s.B == 128) return launch_fwd<128, 128>(s, q, k, v, ids, scale, out, lse, ws, st);
-    return hipErrorInvalidValue;
+    if (!((s.d == 64 || s.d == 128) && (s.B == 64 || s.B == 128))) return hipErrorInvalidValue;
+    // The rows in chunks that keep the workspace under the cap; each chunk
+    // builds its own lists and merges its own rows.
+    const int per = block_prefill_chunk_rows(s);
+    for (int r0 = 0; r0 < s.total_q; r0 += per) {
+        Shape c = s;
+        c.row0 = r0;
+        c.rows = std::min(per, s.total_q - r0);
+        hipError_t e = hipErrorInvalidValue;
+        if (s.d == 64 && s.B == 64) e = launch_fwd<64, 64>(c, q, k, v, ids, scale, out, lse, ws, st);
+        if (s.d == 64 && s.B == 128) e = launch_fwd<64, 128>(c, q, k, v, ids, scale, out, lse, ws, st);
+        if (s.d == 128 && s.B == 64) e = launch_fwd<128, 64>(c, q, k, v, ids, scale, out, lse, ws, st);
+        if (s.d == 128 && s.B == 128) e = launch_fwd<128, 128>(c, q, k, v, ids, scale, out, lse, ws, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace msa

@@ -7,7 +7,9 @@
 // page, section 3.1, its third kernel).
 //
 // Keys are g * nb_max + blk_off[s] + j (j = block of sequence s) and list
-// entries are row * top_k + slot, built in four passes: block offsets of the
+// entries are (row - row0) * top_k + slot for the rows [row0, row0 + rows) of
+// one chunk (the whole problem unless the caller splits it), built in four
+// passes: block offsets of the
 // sequences, a count whose atomics also give each selection its place in its
 // list, an exclusive scan of the counts, and a scatter.  The place a
 // selection gets depends on the order the atomics run in, so list order is
@@ -53,19 +55,21 @@ __global__ __launch_bounds__(kScanThreads) void lists_block_offsets(const int32_
     }
 }
 
-// Key of selection element e = (row * h + g) * top_k + a: g * nb_max +
+// Key of selection element e = (rr * h + g) * top_k + a of the chunk (rr =
+// row - row0; `ids` points at the chunk's first row): g * nb_max +
 // blk_off[s] + j for the block j in that slot, or -1 when the slot is empty or
-// the block is not visible to the row.  *entry receives row * top_k + a.
+// the block is not visible to the row.  *entry receives rr * top_k + a.
 // Threads take consecutive elements, so the reads of the ids (and of `place`)
 // are coalesced.
 __device__ __forceinline__ int selection_key(const int32_t *__restrict__ ids, long e,
                                              const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
                                              const int32_t *__restrict__ blk_off, int num_seqs, int h, int B,
-                                             int top_k, int nb_max, int *entry) {
+                                             int top_k, int nb_max, int row0, int *entry) {
     const long pair = e / top_k;
     const int a = (int)(e - pair * top_k);
-    const int row = (int)(pair / h), g = (int)(pair - (long)row * h);
-    *entry = row * top_k + a;
+    const int rr = (int)(pair / h), g = (int)(pair - (long)rr * h);
+    const int row = row0 + rr;
+    *entry = rr * top_k + a;
     const int j = ids[e];
     if (j < 0) return -1;
     const int s = seq_of_row(cu_q, num_seqs, row);
@@ -80,12 +84,12 @@ __device__ __forceinline__ int selection_key(const int32_t *__restrict__ ids, lo
 template <int PASS>
 __global__ __launch_bounds__(256) void lists_invert(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
                                                   const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
-                                                  int num_seqs, int h, int B, int top_k, int nb_max, long n,
+                                                  int num_seqs, int h, int B, int top_k, int nb_max, int row0, long n,
                                                   int32_t *__restrict__ cnt, int32_t *__restrict__ place,
                                                   const int32_t *__restrict__ off, int32_t *__restrict__ entries) {
     for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
         int entry;
-        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, &entry);
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, &entry);
         if (key < 0) continue;
         if (PASS == 0)
             place[e] = atomicAdd(&cnt[key], 1);
@@ -104,7 +108,7 @@ constexpr int kCountThreads = 1024;   // wide workgroups: the histogram's LDS ca
 __global__ __launch_bounds__(kCountThreads) void lists_count_lds(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
                                                      const int32_t *__restrict__ cu_k,
                                                      const int32_t *__restrict__ blk_off, int num_seqs, int h, int B,
-                                                     int top_k, int nb_max, int keys, long n, long chunk,
+                                                     int top_k, int nb_max, int row0, int keys, long n, long chunk,
                                                      int32_t *__restrict__ cnt, int32_t *__restrict__ place) {
     extern __shared__ int hist[];  // keys entries
     for (int x = threadIdx.x; x < keys; x += kCountThreads) hist[x] = 0;
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(kCountThreads) void lists_count_lds(const int32_t *
     const long e0 = (long)blockIdx.x * chunk, e1 = e0 + chunk < n ? e0 + chunk : n;
     for (long e = e0 + threadIdx.x; e < e1; e += kCountThreads) {
         int entry;
-        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, &entry);
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, &entry);
         if (key >= 0) place[e] = atomicAdd(&hist[key], 1);
     }
     __syncthreads();
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(kCountThreads) void lists_count_lds(const int32_t *
     __syncthreads();
     for (long e = e0 + threadIdx.x; e < e1; e += kCountThreads) {
         int entry;
-        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, &entry);
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, &entry);
         if (key >= 0) place[e] += hist[key];
     }
 }
@@ -177,9 +181,9 @@ BlockLists block_lists_layout(const Shape &s) {
     w.off = at;
     at += al256(((size_t)s.h * w.nb_max + 1) * sizeof(int32_t));
     w.entries = at;
-    at += al256((size_t)s.total_q * s.h * s.top_k * sizeof(int32_t));
+    at += al256((size_t)s.rows * s.h * s.top_k * sizeof(int32_t));
     w.place = at;
-    at += al256((size_t)s.total_q * s.h * s.top_k * sizeof(int32_t));
+    at += al256((size_t)s.rows * s.h * s.top_k * sizeof(int32_t));
     w.bytes = at;
     return w;
 }
@@ -191,7 +195,8 @@ hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLis
     int32_t *entries = reinterpret_cast<int32_t *>(base + w.entries);
     int32_t *place = reinterpret_cast<int32_t *>(base + w.place);
     const long keys = (long)s.h * w.nb_max;
-    const long n = (long)s.total_q * s.h * s.top_k;   // selection elements
+    const long n = (long)s.rows * s.h * s.top_k;   // selection elements of the chunk
+    ids += (size_t)s.row0 * s.h * s.top_k;
     auto grid_of = [](long m, long per) { return dim3((unsigned)((m + per - 1) / per)); };
     const dim3 zgrid = grid_of(std::min(keys, 1L << 22), 256);
     const dim3 egrid = grid_of(std::min(n, 16384L * 256), 256);   // grid-stride over the elements
@@ -203,16 +208,16 @@ hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLis
         const long wgs = std::min(512L, (n + 4095) / 4096);
         const long chunk = ((n + wgs - 1) / wgs + kCountThreads - 1) / kCountThreads * kCountThreads;
         hipLaunchKernelGGL(lists_count_lds, grid_of(n, chunk), dim3(kCountThreads), (size_t)keys * sizeof(int), st, ids, s.cu_q,
-                           s.cu_k, blk_off, s.num_seqs, s.h, s.B, s.top_k, (int)w.nb_max, (int)keys, n, chunk, cnt,
-                           place);
+                           s.cu_k, blk_off, s.num_seqs, s.h, s.B, s.top_k, (int)w.nb_max, s.row0, (int)keys, n, chunk,
+                           cnt, place);
     } else if (n > 0) {
         hipLaunchKernelGGL((lists_invert<0>), egrid, dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off, s.num_seqs, s.h,
-                           s.B, s.top_k, (int)w.nb_max, n, cnt, place, nullptr, nullptr);
+                           s.B, s.top_k, (int)w.nb_max, s.row0, n, cnt, place, nullptr, nullptr);
     }
     hipLaunchKernelGGL(lists_scan, dim3(1), dim3(kScanThreads), 0, st, cnt, keys, off);
     if (n > 0)
         hipLaunchKernelGGL((lists_invert<1>), egrid, dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off, s.num_seqs, s.h,
-                           s.B, s.top_k, (int)w.nb_max, n, cnt, place, off, entries);
+                           s.B, s.top_k, (int)w.nb_max, s.row0, n, cnt, place, off, entries);
     return hipGetLastError();
 }
 

@@ -31,7 +31,9 @@ template <int DI, int B>
 __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int h,
-    float *__restrict__ scores, int e_stride) {
+    float *__restrict__ scores, int e_stride, int row0, int row1) {
+    // Only the packed rows [row0, row1) are scored; scores holds their rows
+    // from row0 on.
     constexpr int ROWB = DI * 2 + 16;          // padded LDS row (bytes)
     constexpr int KS = DI / 16;                // 16-dim k-steps
     constexpr int MT = B / 32;                 // 32-key tiles per block
@@ -50,6 +52,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
     const int tile = gridDim.x - 1 - blockIdx.x;   // heaviest (latest) tiles first
     const int r0 = tile * tq;
     if (r0 >= len_q) return;
+    if (q_begin + r0 >= row1 || q_begin + min(r0 + tq, len_q) <= row0) return;   // no row of the chunk
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
         const int r = r0 + wave * qw + c / h;
         const int g = c % h;
         const bool ok = (c < qw * h) && (r < len_q);
-        col_p[nt] = ok ? shift + r : -1;
+        col_p[nt] = ok ? shift + r : -1;   // rows outside the chunk are scored but not written
         const uint16_t *src = q_idx + ((size_t)(q_begin + r) * h + g) * DI + 8 * (lane >> 5);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = as_bf16x8(load16_if(src + 16 * ks, ok, q_idx));
@@ -154,11 +157,11 @@ __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
             const int c = lane;
             const int r = r0 + wave * qw + c / h;
             const int g = c % h;
-            if (c < qw * h && r < len_q) {
+            if (c < qw * h && r < len_q && q_begin + r >= row0 && q_begin + r < row1) {
                 const int E = (shift + r) / B + 1;
                 const int j0 = j - slot;
                 const int n = min(kStage, E - j0);
-                float *dst = scores + ((size_t)(q_begin + r) * h + g) * e_stride + j0;
+                float *dst = scores + ((size_t)(q_begin + r - row0) * h + g) * e_stride + j0;
                 const float *src = stage[wave][c];
                 if (n == kStage) {
 #pragma unroll
@@ -186,7 +189,7 @@ hipError_t launch(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx, 
     const int tq = (kCols / s.h) * kWaves;
     dim3 grid((s.max_q + tq - 1) / tq, s.num_seqs);
     hipLaunchKernelGGL((index_prefill_blockmax<DI, B>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q, s.cu_k,
-                       s.h, scores, score_stride(s));
+                       s.h, scores, score_stride(s), s.row0, s.row0 + s.rows);
     return hipGetLastError();
 }
 

@@ -33,6 +33,35 @@ msa_status_t check_problem(const msa_problem_t *p) {
     return MSA_SUCCESS;
 }
 
+}  // namespace
+
+namespace msa {
+
+size_t workspace_cap() {
+    const char *e = getenv("MSA_DEBUG_WORKSPACE_CAP");
+    if (e != nullptr && *e != 0) {
+        char *end = nullptr;
+        const unsigned long long v = strtoull(e, &end, 10);
+        if (*end == 0 && v > 0) return (size_t)v;
+    }
+    return MSA_WORKSPACE_CAP_BYTES;
+}
+
+int chunk_rows(const Shape &s, size_t fixed, size_t per_row) {
+    const size_t cap = workspace_cap();
+    const size_t avail = cap > fixed ? cap - fixed : 0;
+    size_t r = per_row > 0 ? avail / per_row : (size_t)s.total_q;
+    // list entries are (row - row0) * top_k + slot in an int
+    const size_t lim = (size_t)0x7fffffff / (size_t)(s.top_k > 0 ? s.top_k : 1);
+    if (r > lim) r = lim;
+    if (r > (size_t)s.total_q) r = (size_t)s.total_q;
+    return r < 1 ? 1 : (int)r;
+}
+
+}  // namespace msa
+
+namespace {
+
 Shape to_shape(const msa_problem_t &p) {
     Shape s;
     s.num_seqs = p.num_seqs;
@@ -48,6 +77,8 @@ Shape to_shape(const msa_problem_t &p) {
     s.top_k = p.top_k;
     s.cu_q = p.cu_seqlens_q;
     s.cu_k = p.cu_seqlens_k;
+    s.row0 = 0;
+    s.rows = p.total_q;
     return s;
 }
 
@@ -66,9 +97,22 @@ msa_status_t attn_support(const msa_problem_t &p) {
     return MSA_SUCCESS;
 }
 
+// One query per sequence: the bandwidth-bound decode scan (it takes the
+// last query of every sequence, so it needs exactly one per sequence).
+bool index_is_decode(const msa_problem_t &p) { return p.max_seqlen_q == 1 && p.total_q == p.num_seqs; }
+
+// Rows per chunk of the index branch: the block scores of a chunk's rows sit
+// in the workspace between the scoring and the select kernel.
+int index_chunk_rows(const msa_problem_t &p) {
+    const Shape s = to_shape(p);
+    if (index_is_decode(p)) return p.total_q;
+    return msa::chunk_rows(s, 0, (size_t)p.num_kv_heads * msa::score_stride(s) * sizeof(float));
+}
+
 size_t index_ws(const msa_problem_t &p) {
     Shape s = to_shape(p);
-    return (size_t)p.total_q * p.num_kv_heads * (size_t)msa::score_stride(s) * sizeof(float);
+    if (p.total_q == 0) return 0;
+    return (size_t)index_chunk_rows(p) * p.num_kv_heads * (size_t)msa::score_stride(s) * sizeof(float);
 }
 
 msa_status_t check_ws(void *ws, size_t have, size_t need) {
@@ -212,7 +256,6 @@ msa_status_t prefill_call(Schedule which, const msa_problem_t *problem, const ms
     if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
     if ((st = attn_support(p)) != MSA_SUCCESS) return st;
     const Shape s = to_shape(p);
-    if (which == Schedule::kBlocks && (long long)p.total_q * p.top_k > 0x7fffffffLL) return MSA_ERROR_NOT_SUPPORTED;
     const bool blocks = which == Schedule::kBlocks || (which == Schedule::kAuto && msa::prefill_prefers_blocks(s));
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     if (debug_validate_on() && (st = debug_validate(p, topk_ids, hs)) != MSA_SUCCESS) return st;
@@ -367,15 +410,23 @@ msa_status_t msa_index_topk_ex(const msa_problem_t *problem, const msa_select_op
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     if (debug_validate_on() && (st = debug_validate(p, nullptr, hs)) != MSA_SUCCESS) return st;
     float *scores = reinterpret_cast<float *>(workspace);
-    // The decode scan takes the last query of every sequence, so it needs
-    // exactly one query per sequence; a batch with empty sequences (fewer
-    // queries than sequences) goes through the prefill kernel, which skips
-    // them.  (The paged path has already required total_q == num_seqs.)
-    const bool decode = p.max_seqlen_q == 1 && p.total_q == p.num_seqs;
-    hipError_t e = decode ? msa::launch_index_decode(s, q_idx, k_idx, scores, hs)
-                          : msa::launch_index_prefill(s, q_idx, k_idx, scores, hs);
-    if (e != hipSuccess) return MSA_ERROR_LAUNCH;
-    return launched(msa::launch_topk_select(s, scores, topk_ids, hs));
+    // A batch with empty sequences (fewer queries than sequences) goes
+    // through the prefill kernel, which skips them.  (The paged path has
+    // already required total_q == num_seqs.)
+    if (index_is_decode(p)) {
+        if (msa::launch_index_decode(s, q_idx, k_idx, scores, hs) != hipSuccess) return MSA_ERROR_LAUNCH;
+        return launched(msa::launch_topk_select(s, scores, topk_ids, hs));
+    }
+    // Prefill: the rows in chunks whose block scores fit the workspace cap.
+    const int per = index_chunk_rows(p);
+    for (int r0 = 0; r0 < p.total_q; r0 += per) {
+        Shape c = s;
+        c.row0 = r0;
+        c.rows = p.total_q - r0 < per ? p.total_q - r0 : per;
+        if (msa::launch_index_prefill(c, q_idx, k_idx, scores, hs) != hipSuccess) return MSA_ERROR_LAUNCH;
+        if (msa::launch_topk_select(c, scores, topk_ids, hs) != hipSuccess) return MSA_ERROR_LAUNCH;
+    }
+    return MSA_SUCCESS;
 }
 
 msa_status_t msa_sparse_attn_decode_paged(const msa_problem_t *problem, const msa_paged_kv_t *paged,

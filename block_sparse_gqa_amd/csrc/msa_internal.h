@@ -18,9 +18,23 @@ struct Shape {
     // Forced blocks in every selection: the first `sink` and the last `local`
     // eligible blocks (0, 0 = plain TopK).
     int sink = 0, local = 0;
+    // The packed query rows [row0, row0 + rows) a launch covers: the entry
+    // points split a problem whose workspace would exceed the cap into such
+    // chunks (positions and key ranges still come from the whole problem's
+    // cu_seqlens).  The whole problem by default.
+    int row0 = 0, rows = 0;
 };
 
-// Block-level scores workspace: [total_q, h, e_stride] float32.
+// Workspace cap per call: the size an entry point splits its query rows to
+// stay under (MSA_WORKSPACE_CAP_BYTES, or the debugging override
+// MSA_DEBUG_WORKSPACE_CAP when that is set to a positive byte count).
+size_t workspace_cap();
+// Query rows per chunk for a per-row workspace cost `per_row` on top of a
+// fixed part `fixed` (at least 1, at most total_q).
+int chunk_rows(const Shape &s, size_t fixed, size_t per_row);
+
+// Block-level scores workspace: [rows, h, e_stride] float32 (the rows of one
+// chunk).
 inline int score_stride(const Shape &s) {
     int e = (s.max_k + s.B - 1) / s.B;
     return (e + 3) / 4 * 4;
@@ -49,6 +63,7 @@ int prefill_tile_queries(const Shape &s);
 // partials, log-sum-exp merge), and whether it is the faster of the two for
 // a shape.
 size_t block_prefill_workspace_bytes(const Shape &s);
+int block_prefill_chunk_rows(const Shape &s);
 bool prefill_prefers_blocks(const Shape &s);
 hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,

@@ -89,11 +89,13 @@ __device__ __forceinline__ int wave_sum(int x) {
 template <int VPT>
 __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict__ scores, int e_stride,
                                                         const int32_t *__restrict__ cu_q,
-                                                        const int32_t *__restrict__ cu_k, int num_seqs, int total_q,
-                                                        int h, int B, int k, int sink, int local,
+                                                        const int32_t *__restrict__ cu_k, int num_seqs, int row0,
+                                                        int rows, int h, int B, int k, int sink, int local,
                                                         int32_t *__restrict__ ids) {
-    const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pair >= (long)total_q * h) return;   // uniform per wave
+    // (row, group) pairs of the rows [row0, row0 + rows); scores holds those rows
+    const long pr = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pr >= (long)rows * h) return;   // uniform per wave
+    const long pair = (long)row0 * h + pr;
     const int t = threadIdx.x & 63;
     const RowInfo ri = row_info(pair, cu_q, cu_k, num_seqs, h, B);
     const int E = ri.E;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict_
         return;
     }
     uint32_t key[VPT];
-    load_keys<VPT>(key, scores + pair * e_stride, t, E, sink, local);
+    load_keys<VPT>(key, scores + pr * e_stride, t, E, sink, local);
 
     // common prefix of the largest and smallest valid key
     uint32_t mx = 0u, mn = 0xffffffffu;
@@ -197,7 +199,7 @@ __device__ __forceinline__ int block_excl_scan(int x, int *red) {
 template <int VPT>
 __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict__ scores, int e_stride,
                                                          const int32_t *__restrict__ cu_q,
-                                                         const int32_t *__restrict__ cu_k, int num_seqs, int total_q,
+                                                         const int32_t *__restrict__ cu_k, int num_seqs, int row0,
                                                          int h, int B, int k, int sink, int local,
                                                          int32_t *__restrict__ ids) {
     __shared__ int hist[kBins];
@@ -205,7 +207,8 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
     __shared__ uint32_t bc[4];
     __shared__ int exact;
 
-    const long pair = blockIdx.x;
+    const long pr = blockIdx.x;                 // pair within the rows from row0 (scores holds those)
+    const long pair = (long)row0 * h + pr;
     const int t = threadIdx.x;
     const RowInfo ri = row_info(pair, cu_q, cu_k, num_seqs, h, B);
     const int E = ri.E;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
         return;
     }
     uint32_t key[VPT];
-    load_keys<VPT>(key, scores + pair * e_stride, t, E, sink, local);
+    load_keys<VPT>(key, scores + pr * e_stride, t, E, sink, local);
 
     uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
@@ -318,18 +321,18 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
 
 template <int VPT>
 hipError_t launch_wave(const Shape &s, const float *scores, int32_t *ids, hipStream_t st) {
-    const long pairs = (long)s.total_q * s.h;
+    const long pairs = (long)s.rows * s.h;
     hipLaunchKernelGGL((topk_select_wave<VPT>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, scores,
-                       score_stride(s), s.cu_q, s.cu_k, s.num_seqs, s.total_q, s.h, s.B, s.top_k, s.sink, s.local,
-                       ids);
+                       score_stride(s), s.cu_q, s.cu_k, s.num_seqs, s.row0, s.rows, s.h, s.B, s.top_k, s.sink,
+                       s.local, ids);
     return hipGetLastError();
 }
 
 template <int VPT>
 hipError_t launch_block(const Shape &s, const float *scores, int32_t *ids, hipStream_t st) {
-    const long pairs = (long)s.total_q * s.h;
+    const long pairs = (long)s.rows * s.h;
     hipLaunchKernelGGL((topk_select_block<VPT>), dim3((unsigned)pairs), dim3(kNT), 0, st, scores, score_stride(s),
-                       s.cu_q, s.cu_k, s.num_seqs, s.total_q, s.h, s.B, s.top_k, s.sink, s.local, ids);
+                       s.cu_q, s.cu_k, s.num_seqs, s.row0, s.h, s.B, s.top_k, s.sink, s.local, ids);
     return hipGetLastError();
 }
 

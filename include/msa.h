@@ -45,6 +45,18 @@
  *    if they break the contract.  No C++ exception crosses the ABI.
  *  - Supported shapes: d in {64, 128}; d_idx in {32, 64}; B in {64, 128};
  *    1 <= H/h <= 16; h <= 64; 1 <= top_k <= 4096.
+ *  - Workspaces are bounded: where a workspace grows with the number of query
+ *    rows (the index branch's block scores, the block-centric schedule's
+ *    lists and partial outputs, the backward's lists and dq partials), the
+ *    call splits the rows into chunks processed one after another, so that
+ *    msa_workspace_size stays at or below MSA_WORKSPACE_CAP_BYTES.  Parts
+ *    that do not grow with the rows stay whole: the block-centric lists'
+ *    per-block counts, the backward's dO.O per row and, when it runs in
+ *    several chunks, its float32 dk and dv accumulators (8 total_k h d
+ *    bytes); the query-tile schedule's workspace is a copy of V.  A chunk has
+ *    at least one row, so a problem whose single row needs more than the cap
+ *    still runs, with a workspace of that size.  Results do not depend on the
+ *    chunking, up to the order of float32 additions in dk and dv.
  */
 #ifndef MSA_H
 #define MSA_H
@@ -55,6 +67,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The workspace cap (see the conventions above): 8 GiB. */
+#define MSA_WORKSPACE_CAP_BYTES ((size_t)8 << 30)
 
 typedef uint16_t msa_bf16_t; /* raw bfloat16 bits */
 typedef void *msa_stream_t;  /* a hipStream_t; NULL = the null stream */

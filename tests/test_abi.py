@@ -338,3 +338,41 @@ def test_validate_host_ids(lib):
     ids2[0, 1, 1] = 1
     ids2[0, 0, 1] = 1
     assert msa.msa_validate_host(p, cu(lq), cu(lk), ids2) == ok
+
+
+CAP = 8 << 30
+
+
+def test_workspaces_stay_under_the_cap(lib, monkeypatch):
+    """The ops whose workspace grows with the query rows split them into chunks, so msa_workspace_size
+    stays under MSA_WORKSPACE_CAP_BYTES; MSA_DEBUG_WORKSPACE_CAP lowers the cap."""
+    monkeypatch.delenv("MSA_DEBUG_WORKSPACE_CAP", raising=False)
+    # a 1M-token causal prefill (the pages' 1M-token figure), H=64, h=8, B=64, k=1024
+    big = prob(total_q=1 << 20, total_k=1 << 20, max_seqlen_q=1 << 20, max_seqlen_k=1 << 20, num_heads=64,
+               num_kv_heads=8, top_k=1024)
+    for op in (msa.MSA_OP_INDEX_TOPK, msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS):
+        n = lib.msa_workspace_size(op, ctypes.byref(big))
+        assert 0 < n <= CAP, (op, n)
+    # the backward keeps float32 dk and dv beside its chunks
+    kv = 8 * (1 << 20) * 8 * 128
+    n = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_BACKWARD, ctypes.byref(big))
+    assert kv < n <= CAP + kv
+    # the 4-sequence ragged prefill (217,091 tokens, H=48, h=8, B=128, k=16): its block-centric workspace was
+    # 44 GB in one piece
+    rag = prob(num_seqs=4, total_q=217091, total_k=217091, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,
+               num_kv_heads=8, block_size=128, top_k=16)
+    for op in (msa.MSA_OP_INDEX_TOPK, msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, msa.MSA_OP_SPARSE_ATTN_PREFILL):
+        assert 0 < lib.msa_workspace_size(op, ctypes.byref(rag)) <= CAP
+    # small problems are not split: the index workspace is every row's block scores
+    p32k = prob(total_q=32768, total_k=32768, max_seqlen_q=32768, max_seqlen_k=32768, num_heads=32, num_kv_heads=8,
+                top_k=32)
+    assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p32k)) == 32768 * 8 * 512 * 4
+    # a lower cap through the debugging override: the same problem in chunks of 8192 rows
+    monkeypatch.setenv("MSA_DEBUG_WORKSPACE_CAP", str(8192 * 8 * 512 * 4))
+    assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p32k)) == 8192 * 8 * 512 * 4
+    small = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(p32k))
+    assert small <= 8192 * 8 * 512 * 4
+    # a decode batch keeps its (small) scores whole
+    d = prob(num_seqs=4, total_q=4, max_seqlen_q=1, total_k=4 << 20, max_seqlen_k=1 << 20, num_heads=64,
+             num_kv_heads=8, top_k=1024)
+    assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(d)) == 4 * 8 * 16384 * 4
