@@ -147,6 +147,7 @@ const char *msa_status_string(msa_status_t status) {
         case MSA_ERROR_NOT_SUPPORTED: return "shape not supported";
         case MSA_ERROR_WORKSPACE: return "workspace missing or too small";
         case MSA_ERROR_LAUNCH: return "kernel launch failed";
+        default: break;
     }
     return "unknown status";
 }

@@ -79,7 +79,10 @@ typedef enum {
     MSA_ERROR_INVALID_VALUE = 1, /* null pointer, inconsistent sizes, H % h != 0, ... */
     MSA_ERROR_NOT_SUPPORTED = 2, /* a shape outside the supported set above */
     MSA_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than msa_workspace_size() */
-    MSA_ERROR_LAUNCH = 4         /* a kernel launch failed */
+    MSA_ERROR_LAUNCH = 4,        /* a kernel launch failed */
+    /* not a status: makes every non-negative 32-bit value a valid
+     * msa_status_t, so msa_status_string may be handed any code */
+    MSA_STATUS_RANGE_ = 0x7fffffff
 } msa_status_t;
 
 typedef enum {

@@ -130,6 +130,37 @@ def test_topk_equals_bruteforce_lexsort(oracle_lib, case):
     assert tie.any(), "integer scores should produce exact ties"
 
 
+@pytest.mark.parametrize("case", [((300,), (300,), 2, 8, 16), ((97, 1, 160), (97, 33, 160), 3, 4, 16),
+                                  ((1, 1), (500, 257), 2, 8, 32), ((70,), (70,), 1, 4, 64)])
+def test_block_scores_equal_bruteforce_maxima(oracle_lib, case):
+    """The oracle's Block Max Pool of one (row, group), value by value, against exact block maxima of
+    integer-valued scores (so float64 and float32 agree exactly): causal rows, a diagonal block cut at
+    the row's position, partial last blocks, decode rows and ragged packing.  Scores of 0 must come
+    back as +0.0 whatever the sign of the products' zero."""
+    sq, sk, h, di, B = case
+    rng = np.random.default_rng(11)
+    tq, tk = sum(sq), sum(sk)
+    q_idx = rng.integers(-3, 4, size=(tq, h, di)).astype(np.float32)
+    k_idx = rng.integers(-3, 4, size=(tk, di)).astype(np.float32)
+    k_idx[::5] = -0.0                     # rows of negative zeros: products -0.0 * x
+    inp = make(sq, sk, h * 2, h, 16, di, B, 2, q_idx=q_idx, k_idx=k_idx)
+    qi, ki = f64(inp.q_idx), f64(inp.k_idx)
+    checked = 0
+    for s in range(len(sq)):
+        q0, k0 = inp.cu_seqlens_q[s], inp.cu_seqlens_k[s]
+        lq, lk = sq[s], sk[s]
+        for r in range(lq):
+            p = lk - lq + r
+            for g in range(h):
+                sc = ki[k0:k0 + p + 1] @ qi[q0 + r, g]
+                ref = np.array([sc[j * B:min((j + 1) * B, p + 1)].max() for j in range(p // B + 1)])
+                got = oracle_lib.block_scores(inp, int(q0 + r), g)
+                np.testing.assert_array_equal(got, ref.astype(np.float32))
+                assert not np.signbit(got[got == 0]).any()
+                checked += 1
+    assert checked == tq * h
+
+
 def _planted(n, h, B, K, values, di=8):
     """Q_idx[., g] = e_g; K_idx zero except one planted token per (group, block)."""
     q_idx = np.zeros((n, h, di), np.float32)
