@@ -12,8 +12,8 @@
 // the MFMA M dimension (v_mfma_f32_32x32x16_bf16): each lane then holds one
 // column and 16 keys of a 32-key tile, the block max is an in-register max
 // plus one permlane32 swap.  K_idx tiles are double-buffered in LDS; the
-// block scores of 16 consecutive blocks are staged in LDS and written to the
-// [row, group, block] workspace as contiguous runs.
+// block scores of 32 consecutive blocks are staged in LDS and written to the
+// [row, group, block] workspace as contiguous 128-byte runs (whole lines).
 #include <type_traits>
 
 #include "msa_device.h"
@@ -25,7 +25,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kCols = 64;     // columns per wave
-constexpr int kStage = 16;    // blocks per staged flush
+constexpr int kStage = 32;    // blocks per staged flush: one 128-byte line of scores per column
 
 template <int DI, int B>
 __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(

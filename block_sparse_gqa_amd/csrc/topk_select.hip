@@ -21,6 +21,7 @@
 // with an LDS histogram and a suffix scan.
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_select.h"
 
 namespace msa {
 
@@ -47,44 +48,6 @@ __device__ __forceinline__ RowInfo row_info(long pair, const int32_t *cu_q, cons
     return RowInfo{p / B + 1, pair};
 }
 
-// Keys of blocks t*VPT .. t*VPT+VPT-1 (0 past E).  Forced blocks (the first
-// `sink` and the last `local` eligible ones) get the largest key, above that
-// of any score, so they are always kept; the caller guarantees
-// sink + local <= k.
-template <int VPT>
-__device__ __forceinline__ void load_keys(uint32_t (&key)[VPT], const float *src, int t, int E, int sink, int local) {
-#pragma unroll
-    for (int v = 0; v < VPT; v += 4) {
-        const int i = t * VPT + v;
-        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < E) f = *reinterpret_cast<const float4 *>(src + i);
-        const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = i + u;
-            key[v + u] = (j < E) ? ((j < sink || j >= E - local) ? 0xffffffffu : order_key(fv[u])) : 0u;
-        }
-    }
-}
-
-// Wave-level exclusive prefix sum (lane order).
-__device__ __forceinline__ int wave_excl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-    }
-    return incl - x;
-}
-
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
 // ---------------------------------------------------------------- one wave
 template <int VPT>
 __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict__ scores, int e_stride,
@@ -104,69 +67,7 @@ __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict_
         for (int x = t; x < k; x += 64) out[x] = x < E ? x : -1;
         return;
     }
-    uint32_t key[VPT];
-    load_keys<VPT>(key, scores + pr * e_stride, t, E, sink, local);
-
-    // common prefix of the largest and smallest valid key
-    uint32_t mx = 0u, mn = 0xffffffffu;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        mx = max(mx, key[v]);
-        mn = min(mn, key[v] ? key[v] : 0xffffffffu);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-    }
-    // Equal in every lane after the butterfly; reading them into scalar
-    // registers makes the search below scalar-controlled (no exec-mask
-    // bookkeeping per step, the candidate is a scalar operand of the compares).
-    mx = __builtin_amdgcn_readfirstlane(mx);
-    mn = __builtin_amdgcn_readfirstlane(mn);
-    // T = largest value with count(key >= T) >= k (the k-th largest key).  All
-    // valid keys share the bits above `top`; start there with zeros below.
-    const int top = (mx == mn) ? -1 : 31 - __builtin_clz(mx ^ mn);
-    uint32_t T = (top < 0) ? mx : (mx & ~((2u << top) - 1u));
-    for (int bit = top; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        int c = 0;
-#pragma unroll
-        for (int v = 0; v < VPT; ++v) c += __builtin_popcountll(__ballot(key[v] >= cand));
-        if (c >= k) T = cand;
-        if (c == k) {
-            // exactly k keys are >= cand: they are the selection (the k-th and
-            // (k+1)-th largest keys are on opposite sides of cand, so no tie
-            // crosses the boundary); lowering T to cand - 1 keeps every one of
-            // them "> T" below
-            T = cand - 1u;
-            break;
-        }
-    }
-    int n_gt = 0, n_eq = 0;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        n_gt += key[v] > T;
-        n_eq += key[v] == T;
-    }
-    const int need_eq = k - wave_sum(n_gt);
-    int eq_seen = wave_excl_scan(n_eq);
-    int sel = 0;
-    bool take[VPT];
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        bool tk = key[v] > T;
-        if (key[v] == T) {
-            tk = eq_seen < need_eq;
-            ++eq_seen;
-        }
-        take[v] = tk;
-        sel += tk;
-    }
-    int pos = wave_excl_scan(sel);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v)
-        if (take[v] && pos < k) out[pos++] = t * VPT + v;
+    wave_topk_row<VPT>(scores + pr * e_stride, E, k, sink, local, out);
 }
 
 // ---------------------------------------------------------------- workgroup
