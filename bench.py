@@ -154,31 +154,45 @@ def cpu_baseline(inputs, budget_s=24.0, seed=7):
             "sample": "; ".join(parts) + "; each part extrapolated linearly to its full workload"}
 
 
-def measured_traffic(kernel_file, symbol, launches_per_call, workload):
-    """HBM bytes per call of the dominant kernel from the committed PMC summary.
+# The kernels one msa_sparse_attn_prefill call launches (source file, kernel), per schedule; the
+# block-centric part runs in one chunk at the benchmarked sizes.
+_TILE_KERNELS = [("attn_prefill.hip", "v_absmax_bits"), ("attn_prefill.hip", "v_to_f16"),
+                 ("attn_prefill.hip", "attn_prefill_tile")]
+_BLOCK_KERNELS = [("block_lists.hip", "lists_block_offsets"), ("block_lists.hip", "fill_zero_i32"),
+                  ("block_lists.hip", "lists_count_lds"), ("block_lists.hip", "lists_scan"),
+                  ("block_lists.hip", "lists_invert"), ("attn_block_fwd.hip", "fwd_block"),
+                  ("attn_block_fwd.hip", "fwd_merge")]
+PREFILL_CALL_KERNELS = {"tiles": _TILE_KERNELS, "blocks": _BLOCK_KERNELS, "tiles+blocks": _TILE_KERNELS + _BLOCK_KERNELS}
 
-    The summary records FETCH_SIZE / WRITE_SIZE per dispatch, the scale factors
-    a plain copy of known size gives for the same counters, the SHA-256 of the
-    kernel source the counters were taken on, and the workloads they were
-    taken on.  If that source has changed since, or the workload is another,
-    the counters do not describe this launch and None is returned.
+
+def measured_traffic(kernels, workload):
+    """HBM bytes of one call from the committed PMC summary: the sum over the call's kernels.
+
+    The summary records, per kernel, FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same
+    counters read for a plain copy of known size, the SHA-256 of the kernel source the counters were
+    taken on, and the workloads they were taken on.  If any kernel's source has changed since, or it
+    has no entry for this workload, the counters do not describe this call and None is returned.
     """
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    src = os.path.join(ROOT, "block_sparse_gqa_amd", "csrc", kernel_file)
     try:
         with open(path) as f:
             table = json.load(f)
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if workload not in table.get("workload", "").replace("+", " ").split():
-        return None
-    for e in table.get("kernels", []):
-        if e.get("symbol") == symbol and e.get("source_sha256") == digest:
-            return e["bytes_per_dispatch"] * launches_per_call
-    return None
+    total = 0.0
+    for kernel_file, symbol in kernels:
+        try:
+            with open(os.path.join(ROOT, "block_sparse_gqa_amd", "csrc", kernel_file), "rb") as f:
+                digest = hashlib.sha256(f.read()).hexdigest()
+        except OSError:
+            return None
+        hit = [e for e in table.get("kernels", []) if e.get("symbol") == symbol and
+               e.get("source_sha256") == digest and e.get("workload") == workload]
+        if not hit:
+            return None
+        total += hit[0]["bytes_per_dispatch"]
+    return total
 
 
 def decode_reps(dp, bufs, reps=100, flush_mb=1024):
@@ -314,13 +328,26 @@ def prefill_schedules(dp, bufs, fwd, steps):
         outs[name] = o
         del ws, l
         torch.cuda.empty_cache()
-    need = msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, dp.problem)
-    blocks_need = msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem)
-    res["auto"] = "blocks" if need == blocks_need else "tiles"
+    res["auto"] = prefill_schedule_of(dp)
     res["max_abs_diff"] = float((outs["tiles"].float() - outs["blocks"].float()).abs().max())
     del outs
     torch.cuda.empty_cache()
     return res
+
+
+def prefill_schedule_of(dp):
+    """What msa_sparse_attn_prefill runs for this problem, read from its workspace size: the query tiles,
+    the block-centric schedule, or both (tiles for the early rows, the block-centric schedule after)."""
+    from block_sparse_gqa_amd import msa
+    ws = {op: msa.msa_workspace_size(op, dp.problem) for op in (msa.MSA_OP_SPARSE_ATTN_PREFILL,
+                                                                 msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES,
+                                                                 msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS)}
+    auto = ws[msa.MSA_OP_SPARSE_ATTN_PREFILL]
+    if auto == ws[msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES]:
+        return "tiles"
+    if auto == ws[msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS]:
+        return "blocks"
+    return "tiles+blocks"
 
 
 def summarize(inp, dp, ids, evs):
@@ -351,20 +378,18 @@ def summarize(inp, dp, ids, evs):
         tf_i = alg["index_flops"] / (t_idx * 1e-3) / 1e12
         tf_a = alg["attn_flops"] / (t_att * 1e-3) / 1e12
         tot = (alg["index_flops"] + alg["attn_flops"]) / ((t_idx + t_att) * 1e-3) / 1e12
-        on_blocks = (msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, dp.problem)
-                     == msa.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, dp.problem))
+        schedule = prefill_schedule_of(dp)
         r.update({"bound": "mfma", "algorithmic_TFLOP": (alg["index_flops"] + alg["attn_flops"]) / 1e12,
                   "TFLOP_per_s": tot, "frac_mfma_peak": tot / MFMA_BF16_PEAK_TFLOPS,
                   "index_topk_TFLOP_per_s": tf_i, "sparse_attn_TFLOP_per_s": tf_a,
                   "index_topk_frac_mfma_peak": tf_i / MFMA_BF16_PEAK_TFLOPS,
                   "sparse_attn_frac_mfma_peak": tf_a / MFMA_BF16_PEAK_TFLOPS,
-                  "prefill_schedule": "blocks" if on_blocks else "tiles"})
+                  "prefill_schedule": schedule})
         kernels.append(("msa_index_topk[%s]" % name, t_idx, "mfma", alg["index_flops"], None))
-        # One launch of attn_prefill_tile per call on the query-tile schedule.  The committed
-        # counters cover that kernel on the workloads they name; the block-centric schedule's
-        # three kernels have none, so its traffic stays null.
+        # The call's kernels, for the HBM traffic the committed counters give (null unless they cover
+        # every kernel of the call on this workload, measured on the current sources).
         kernels.append(("msa_sparse_attn_prefill[%s]" % name, t_att, "mfma", alg["attn_flops"],
-                        None if on_blocks else ("attn_prefill.hip", "attn_prefill_tile", 1, name)))
+                        (PREFILL_CALL_KERNELS[schedule], name)))
     return r, kernels
 
 

@@ -31,6 +31,7 @@
 // merge by log-sum-exp into O (bf16) and LSE (natural log) in one pass, in a
 // fixed order; one wave takes the G heads of a (row, group).
 #include <algorithm>
+#include <cmath>
 
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -267,8 +268,8 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ part_o, const float2 *__restrict__ part_w,
                                                  const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
                                                  const int32_t *__restrict__ cu_k, int num_seqs, int row0,
-                                                 long n_pairs, int H, int h, int B, int top_k,
-                                                 uint16_t *__restrict__ out, float *__restrict__ lse) {
+                                                 long n_pairs, int H, int h, int B, int top_k, int blocks_from,
+                                                 int split_tq, uint16_t *__restrict__ out, float *__restrict__ lse) {
     constexpr int CPR = D / 8;       // 16-byte chunks per partial row
     constexpr int HPP = 64 / CPR;    // heads per pass
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -279,6 +280,7 @@ __global__ __launch_bounds__(256) void fwd_merge(const uint16_t *__restrict__ pa
     const int row = row0 + rr;
     const int s = seq_of_row(cu_q, num_seqs, row);
     const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
+    if (blocks_from > p - (row - cu_q[s]) % split_tq) return;   // a row of the query-tile schedule
     const int32_t *sel = ids + ((size_t)row * h + g) * top_k;
     const size_t base = (size_t)rr * top_k;   // the chunk's partials
 
@@ -354,7 +356,8 @@ hipError_t launch_fwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
                        scale * kLog2e, part_o, part_w);
     const long pairs = (long)s.rows * s.h;
     hipLaunchKernelGGL((fwd_merge<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, part_o, part_w, ids, s.cu_q,
-                       s.cu_k, s.num_seqs, s.row0, pairs, s.H, s.h, s.B, s.top_k, out, lse);
+                       s.cu_k, s.num_seqs, s.row0, pairs, s.H, s.h, s.B, s.top_k, s.blocks_from, s.split_tq, out,
+                       lse);
     return hipGetLastError();
 }
 
@@ -378,23 +381,29 @@ size_t block_prefill_workspace_bytes(const Shape &s) {
 
 // The query tiles stage the union of a tile's selections once per tile, so
 // they pay off while a staged block serves many of the tile's queries: about
-// R = Tq k / E_avg of them, with Tq queries per tile and E_avg the eligible
-// blocks of an average query of the longest sequence.  The block-centric
-// schedule does no wasted work but writes and reads back one partial output
-// per (row, slot, head).  Measured on 8K-64K-token prefills with clustered
-// keys, each schedule called on its own (query-tile time / block-centric
-// time): B = 64, G = 4 gave 0.48 at R = 32, 0.71-0.72 at 16, 0.92-0.96 at 8,
-// 1.10 at 6, 1.31-1.32 at 4 and 1.68 at 2; B = 128, G = 6 gave 0.65 at
-// R = 16, 0.89 at 12, 1.05 at 8, 1.22 at 6, 1.49 at 4, 2.13 at 2 and about
-// 7 at about 1 (a 4-sequence 217K-token ragged prefill).  So the switch
-// points are R = 7 (B = 64) and R = 10 (B = 128).
-bool prefill_prefers_blocks(const Shape &s) {
+// R = Tq min(k, E) / E of them for a tile of Tq queries with E eligible
+// blocks.  The block-centric schedule does no wasted work but writes and
+// reads back one partial output per (row, slot, head).  Measured on
+// 8K-64K-token prefills with clustered keys, each schedule called on its own
+// (query-tile time / block-centric time, R taken at the average E): B = 64,
+// G = 4 gave 0.48 at R = 32, 0.71-0.72 at 16, 0.92-0.96 at 8, 1.10 at 6,
+// 1.31-1.32 at 4 and 1.68 at 2; B = 128, G = 6 gave 0.65 at R = 16, 0.89 at
+// 12, 1.05 at 8, 1.22 at 6, 1.49 at 4, 2.13 at 2 and about 7 at about 1 (a
+// 4-sequence 217K-token ragged prefill).  So the schedules break even near
+// R = 7 (B = 64) and R = 10 (B = 128).  The rule is applied per query tile:
+// E grows with the position, so the tiles take the early rows and the
+// block-centric schedule the late ones.  Splitting a 32768-token prefill
+// (B = 64, k = 32, G = 4) at 8K, 12K, 16K, 20K and 24K rows took 4.28, 4.35,
+// 4.12, 4.18 and 4.34 ms, against 4.89 ms on the tiles alone; the switch at
+// R = 8 for B = 64 puts that split at 16384.
+int prefill_split_position(const Shape &s) {
     const int G = s.H / s.h;
-    if (G < 1 || G > 16 || s.max_q < 1) return false;
-    const double e_k = (double)((s.max_k + s.B - 1) / s.B), e_q = (double)((s.max_q + s.B - 1) / s.B);
-    const double e_avg = std::max(1.0, e_k - 0.5 * e_q);
-    const double r = (double)prefill_tile_queries(s) * std::min((double)s.top_k, e_k) / e_avg;
-    return r < (s.B >= 128 ? 10.0 : 7.0);
+    if (G < 1 || G > 16 || s.max_q < 1) return 0x7fffffff;
+    const double thr = s.B >= 128 ? 10.0 : 8.0;
+    // R = Tq k / E < thr  <=>  E > Tq k / thr (with E > k; for E <= k, R = Tq >= 16)
+    const long e_star = (long)std::floor((double)prefill_tile_queries(s) * s.top_k / thr) + 1;
+    const long p = (e_star - 1) * s.B;
+    return p >= 0x7fffffffL ? 0x7fffffff : (int)p;
 }
 
 hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -402,13 +411,14 @@ hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const u
                                       hipStream_t st) {
     if (s.H / s.h > 16) return hipErrorInvalidValue;
     if (!((s.d == 64 || s.d == 128) && (s.B == 64 || s.B == 128))) return hipErrorInvalidValue;
-    // The rows in chunks that keep the workspace under the cap; each chunk
-    // builds its own lists and merges its own rows.
+    // The rows [s.row0, s.row0 + s.rows) in chunks that keep the workspace
+    // under the cap; each chunk builds its own lists and merges its own rows.
     const int per = block_prefill_chunk_rows(s);
-    for (int r0 = 0; r0 < s.total_q; r0 += per) {
+    const int r_end = s.row0 + s.rows;
+    for (int r0 = s.row0; r0 < r_end; r0 += per) {
         Shape c = s;
         c.row0 = r0;
-        c.rows = std::min(per, s.total_q - r0);
+        c.rows = std::min(per, r_end - r0);
         hipError_t e = hipErrorInvalidValue;
         if (s.d == 64 && s.B == 64) e = launch_fwd<64, 64>(c, q, k, v, ids, scale, out, lse, ws, st);
         if (s.d == 64 && s.B == 128) e = launch_fwd<64, 128>(c, q, k, v, ids, scale, out, lse, ws, st);

@@ -36,6 +36,7 @@
 //                     the S^T accumulators.
 // Workgroups are numbered group-fastest, so with 8 groups all tiles of a
 // group run on the same XCD and share its L2.
+#include <algorithm>
 #include <cstdlib>
 
 #include "msa_device.h"
@@ -216,7 +217,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
     int num_seqs, int H, int h, int B, int top_k, int max_tiles, float c2, const int *__restrict__ v_exp,
-    uint16_t *__restrict__ out, float *__restrict__ lse, int spin_limit, unsigned *__restrict__ wait_flag) {
+    uint16_t *__restrict__ out, float *__restrict__ lse, int spin_limit, unsigned *__restrict__ wait_flag,
+    int tiles_below) {
     using R = Ring<D>;
     constexpr int KS = D / 32;
     constexpr int DT = D / 16;
@@ -246,6 +248,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const int r0 = tile * Tq;
     if (r0 >= len_q) return;
     const int shift = len_k - len_q;
+    if (shift + r0 >= tiles_below) return;   // the block-centric schedule's rows
     const int tq_valid = min(Tq, len_q - r0);
     const int p_last = shift + r0 + tq_valid - 1;
     const int e_tile = p_last / B + 1;
@@ -665,12 +668,16 @@ hipError_t launch(const Shape &s, const uint16_t *q, const uint16_t *k, const ui
                   const int32_t *ids, float scale, uint16_t *out, float *lse, unsigned *wait_flag, hipStream_t st) {
     const int G = s.H / s.h;
     const int Tq = NW * (16 / G);
-    const int max_tiles = (s.max_q + Tq - 1) / Tq;
+    // a tile starting at row r0 of a sequence sits at position >= r0, so with
+    // rows split between the schedules no tile at or past tiles_below runs
+    const int rows_max = s.tiles_below < s.max_q ? std::max(s.tiles_below, 0) : s.max_q;
+    const int max_tiles = (rows_max + Tq - 1) / Tq;
+    if (max_tiles == 0) return hipSuccess;
     const long grid = (long)max_tiles * s.num_seqs * s.h;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_prefill_tile<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, q, k, v16, ids, s.cu_q,
                        s.cu_k, s.num_seqs, s.H, s.h, s.B, s.top_k, max_tiles, scale * kLog2e, v_exp, out, lse,
-                       spin_limit_from_env(), wait_flag);
+                       spin_limit_from_env(), wait_flag, s.tiles_below);
     return hipGetLastError();
 }
 

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kScanThreads) void lists_block_offsets(const int32_
 __device__ __forceinline__ int selection_key(const int32_t *__restrict__ ids, long e,
                                              const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
                                              const int32_t *__restrict__ blk_off, int num_seqs, int h, int B,
-                                             int top_k, int nb_max, int row0, int *entry) {
+                                             int top_k, int nb_max, int row0, int blocks_from, int split_tq,
+                                             int *entry) {
     const long pair = e / top_k;
     const int a = (int)(e - pair * top_k);
     const int rr = (int)(pair / h), g = (int)(pair - (long)rr * h);
@@ -73,8 +74,11 @@ __device__ __forceinline__ int selection_key(const int32_t *__restrict__ ids, lo
     const int j = ids[e];
     if (j < 0) return -1;
     const int s = seq_of_row(cu_q, num_seqs, row);
-    const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]) + (row - cu_q[s]);
+    const int shift = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - cu_q[s]);
+    const int p = shift + (row - cu_q[s]);
     if (j > p / B) return -1;
+    // rows of query tiles starting below blocks_from belong to the other schedule
+    if (blocks_from > p - (row - cu_q[s]) % split_tq) return -1;
     return g * nb_max + blk_off[s] + j;
 }
 
@@ -84,12 +88,13 @@ __device__ __forceinline__ int selection_key(const int32_t *__restrict__ ids, lo
 template <int PASS>
 __global__ __launch_bounds__(256) void lists_invert(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
                                                   const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
-                                                  int num_seqs, int h, int B, int top_k, int nb_max, int row0, long n,
+                                                  int num_seqs, int h, int B, int top_k, int nb_max, int row0,
+                                                  int blocks_from, int split_tq, long n,
                                                   int32_t *__restrict__ cnt, int32_t *__restrict__ place,
                                                   const int32_t *__restrict__ off, int32_t *__restrict__ entries) {
     for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
         int entry;
-        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, &entry);
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, blocks_from, split_tq, &entry);
         if (key < 0) continue;
         if (PASS == 0)
             place[e] = atomicAdd(&cnt[key], 1);
@@ -108,7 +113,8 @@ constexpr int kCountThreads = 1024;   // wide workgroups: the histogram's LDS ca
 __global__ __launch_bounds__(kCountThreads) void lists_count_lds(const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q,
                                                      const int32_t *__restrict__ cu_k,
                                                      const int32_t *__restrict__ blk_off, int num_seqs, int h, int B,
-                                                     int top_k, int nb_max, int row0, int keys, long n, long chunk,
+                                                     int top_k, int nb_max, int row0, int blocks_from, int split_tq,
+                                                     int keys, long n, long chunk,
                                                      int32_t *__restrict__ cnt, int32_t *__restrict__ place) {
     extern __shared__ int hist[];  // keys entries
     for (int x = threadIdx.x; x < keys; x += kCountThreads) hist[x] = 0;
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(kCountThreads) void lists_count_lds(const int32_t *
     const long e0 = (long)blockIdx.x * chunk, e1 = e0 + chunk < n ? e0 + chunk : n;
     for (long e = e0 + threadIdx.x; e < e1; e += kCountThreads) {
         int entry;
-        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, &entry);
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, blocks_from, split_tq, &entry);
         if (key >= 0) place[e] = atomicAdd(&hist[key], 1);
     }
     __syncthreads();
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(kCountThreads) void lists_count_lds(const int32_t *
     __syncthreads();
     for (long e = e0 + threadIdx.x; e < e1; e += kCountThreads) {
         int entry;
-        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, &entry);
+        const int key = selection_key(ids, e, cu_q, cu_k, blk_off, num_seqs, h, B, top_k, nb_max, row0, blocks_from, split_tq, &entry);
         if (key >= 0) place[e] += hist[key];
     }
 }
@@ -208,16 +214,18 @@ hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLis
         const long wgs = std::min(512L, (n + 4095) / 4096);
         const long chunk = ((n + wgs - 1) / wgs + kCountThreads - 1) / kCountThreads * kCountThreads;
         hipLaunchKernelGGL(lists_count_lds, grid_of(n, chunk), dim3(kCountThreads), (size_t)keys * sizeof(int), st, ids, s.cu_q,
-                           s.cu_k, blk_off, s.num_seqs, s.h, s.B, s.top_k, (int)w.nb_max, s.row0, (int)keys, n, chunk,
-                           cnt, place);
+                           s.cu_k, blk_off, s.num_seqs, s.h, s.B, s.top_k, (int)w.nb_max, s.row0, s.blocks_from,
+                           s.split_tq, (int)keys, n, chunk, cnt, place);
     } else if (n > 0) {
         hipLaunchKernelGGL((lists_invert<0>), egrid, dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off, s.num_seqs, s.h,
-                           s.B, s.top_k, (int)w.nb_max, s.row0, n, cnt, place, nullptr, nullptr);
+                           s.B, s.top_k, (int)w.nb_max, s.row0, s.blocks_from, s.split_tq, n, cnt, place, nullptr,
+                           nullptr);
     }
     hipLaunchKernelGGL(lists_scan, dim3(1), dim3(kScanThreads), 0, st, cnt, keys, off);
     if (n > 0)
         hipLaunchKernelGGL((lists_invert<1>), egrid, dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off, s.num_seqs, s.h,
-                           s.B, s.top_k, (int)w.nb_max, s.row0, n, cnt, place, off, entries);
+                           s.B, s.top_k, (int)w.nb_max, s.row0, s.blocks_from, s.split_tq, n, cnt, place, off,
+                           entries);
     return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // frees or synchronises; every check runs on the host before any launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <new>
 #include <vector>
@@ -115,6 +116,23 @@ size_t index_ws(const msa_problem_t &p) {
     return (size_t)index_chunk_rows(p) * p.num_kv_heads * (size_t)msa::score_stride(s) * sizeof(float);
 }
 
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The automatic prefill: query tiles for the rows before the split position,
+// the block-centric schedule for the rest (when any row can reach it); the
+// query-tile part's workspace first, then the block-centric part's.
+bool prefill_auto_split(const Shape &s, int *split) {
+    *split = msa::prefill_split_position(s);
+    return *split <= s.max_k - 1;
+}
+
+size_t prefill_auto_ws(const Shape &s) {
+    int split = 0;
+    const size_t tiles = msa::prefill_workspace_bytes(s);
+    if (!prefill_auto_split(s, &split)) return tiles;
+    return al256(tiles) + msa::block_prefill_workspace_bytes(s);
+}
+
 msa_status_t check_ws(void *ws, size_t have, size_t need) {
     if (need == 0) return MSA_SUCCESS;
     if (ws == nullptr || have < need) return MSA_ERROR_WORKSPACE;
@@ -159,12 +177,9 @@ size_t msa_workspace_size(int op, const msa_problem_t *problem) {
         case MSA_OP_INDEX_TOPK:
             if (index_support(p) != MSA_SUCCESS) return (size_t)-1;
             return index_ws(p);
-        case MSA_OP_SPARSE_ATTN_PREFILL: {
+        case MSA_OP_SPARSE_ATTN_PREFILL:
             if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
-            const Shape s = to_shape(p);
-            return msa::prefill_prefers_blocks(s) ? msa::block_prefill_workspace_bytes(s)
-                                                  : msa::prefill_workspace_bytes(s);
-        }
+            return prefill_auto_ws(to_shape(p));
         case MSA_OP_SPARSE_ATTN_PREFILL_TILES:
             if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
             return msa::prefill_workspace_bytes(to_shape(p));
@@ -227,8 +242,7 @@ size_t msa_workspace_wait_word(int op, const msa_problem_t *problem) {
     if (attn_support(p) != MSA_SUCCESS) return (size_t)-1;
     const Shape s = to_shape(p);
     switch (op) {
-        case MSA_OP_SPARSE_ATTN_PREFILL:
-            if (msa::prefill_prefers_blocks(s)) return (size_t)-1;
+        case MSA_OP_SPARSE_ATTN_PREFILL:   // the query-tile part's workspace comes first
             return msa::prefill_wait_word_offset(s);
         case MSA_OP_SPARSE_ATTN_PREFILL_TILES:
             return msa::prefill_wait_word_offset(s);
@@ -245,6 +259,7 @@ namespace {
 // Which prefill schedule a call runs.
 enum class Schedule { kAuto, kTiles, kBlocks };
 
+
 msa_status_t prefill_call(Schedule which, const msa_problem_t *problem, const msa_bf16_t *q, const msa_bf16_t *k,
                           const msa_bf16_t *v, const int32_t *topk_ids, float softmax_scale, msa_bf16_t *out,
                           float *lse, void *workspace, size_t workspace_bytes, msa_stream_t stream) {
@@ -257,16 +272,39 @@ msa_status_t prefill_call(Schedule which, const msa_problem_t *problem, const ms
     if (!(softmax_scale > 0.0f) || softmax_scale == __builtin_inff()) return MSA_ERROR_INVALID_VALUE;
     if ((st = attn_support(p)) != MSA_SUCCESS) return st;
     const Shape s = to_shape(p);
-    const bool blocks = which == Schedule::kBlocks || (which == Schedule::kAuto && msa::prefill_prefers_blocks(s));
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    if (debug_validate_on() && (st = debug_validate(p, topk_ids, hs)) != MSA_SUCCESS) return st;
-    if (blocks) {
+    if (which == Schedule::kBlocks) {
         if ((st = check_ws(workspace, workspace_bytes, msa::block_prefill_workspace_bytes(s))) != MSA_SUCCESS)
             return st;
+        if (debug_validate_on() && (st = debug_validate(p, topk_ids, hs)) != MSA_SUCCESS) return st;
         return launched(msa::launch_attn_prefill_blocks(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs));
     }
-    if ((st = check_ws(workspace, workspace_bytes, msa::prefill_workspace_bytes(s))) != MSA_SUCCESS) return st;
-    return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs));
+    int split = 0;
+    const bool hybrid = which == Schedule::kAuto && prefill_auto_split(s, &split);
+    const size_t need = hybrid ? prefill_auto_ws(s) : msa::prefill_workspace_bytes(s);
+    if ((st = check_ws(workspace, workspace_bytes, need)) != MSA_SUCCESS) return st;
+    if (debug_validate_on() && (st = debug_validate(p, topk_ids, hs)) != MSA_SUCCESS) return st;
+    if (!hybrid) return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs));
+    // rows split by position: the early ones (few eligible blocks) on the
+    // query tiles, the late ones on the block-centric schedule
+    Shape st_tiles = s, st_blocks = s;
+    st_tiles.tiles_below = split;
+    st_blocks.blocks_from = split;
+    st_blocks.split_tq = msa::prefill_tile_queries(s);
+    if (p.num_seqs == 1) {
+        // one sequence: its rows before the first tile that starts at or past
+        // the split (positions are total_k - total_q + row) are all the tiles'
+        const long tq = st_blocks.split_tq;
+        const long first = ((long)split - (p.total_k - p.total_q) + tq - 1) / tq * tq;
+        const int r0 = (int)std::min<long>(std::max<long>(first, 0), p.total_q);
+        st_blocks.row0 = r0;
+        st_blocks.rows = p.total_q - r0;
+    }
+    char *wsb = static_cast<char *>(workspace);
+    if (msa::launch_attn_prefill(st_tiles, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs) != hipSuccess)
+        return MSA_ERROR_LAUNCH;
+    return launched(msa::launch_attn_prefill_blocks(st_blocks, q, k, v, topk_ids, softmax_scale, out, lse,
+                                                    wsb + al256(msa::prefill_workspace_bytes(s)), hs));
 }
 }  // namespace
 

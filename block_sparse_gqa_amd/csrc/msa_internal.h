@@ -23,6 +23,12 @@ struct Shape {
     // chunks (positions and key ranges still come from the whole problem's
     // cu_seqlens).  The whole problem by default.
     int row0 = 0, rows = 0;
+    // Prefill rows split between the two attention schedules: a row whose
+    // query tile (split_tq consecutive queries from its sequence's first)
+    // starts at a position below tiles_below is the query-tile kernel's, one
+    // whose tile starts at or after blocks_from the block-centric path's.
+    // The defaults give every row to whichever schedule is called.
+    int tiles_below = 0x7fffffff, blocks_from = -0x7fffffff - 1, split_tq = 1;
 };
 
 // Workspace cap per call: the size an entry point splits its query rows to
@@ -64,7 +70,10 @@ int prefill_tile_queries(const Shape &s);
 // a shape.
 size_t block_prefill_workspace_bytes(const Shape &s);
 int block_prefill_chunk_rows(const Shape &s);
-bool prefill_prefers_blocks(const Shape &s);
+// Position from which the block-centric schedule beats the query tiles:
+// rows whose query tile starts there or later go to it (<= 0: every row;
+// >= max_seqlen_k: none).
+int prefill_split_position(const Shape &s);
 hipError_t launch_attn_prefill_blocks(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws,
                                       hipStream_t st);

@@ -65,24 +65,29 @@ def test_workspace_size(lib):
     vbytes = p.total_k * p.num_kv_heads * p.head_dim * 2
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p)) == \
         (vbytes + 255) // 256 * 256 + 1024 * 4 + 256
-    # short context, every block selected: the prefill call runs the query tiles
+    # short context, every position before the split (R = Tq k / E >= 7 while E <= 292): the prefill call runs
+    # the query tiles only
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == \
         lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
-    # 131072-token prefill with k = 16 and B = 128: the block-centric schedule
+
+    def both(pp):   # the query tiles' workspace (256-byte aligned), then the block-centric one
+        t = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(pp))
+        return (t + 255) // 256 * 256 + lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(pp))
+
+    # longer contexts split the rows at a position: tiles before it, the block-centric schedule after it
     long_ctx = prob(total_q=131072, total_k=131072, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,
                     num_kv_heads=8, block_size=128, top_k=16)
-    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(long_ctx)) == \
-        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(long_ctx))
-    # the 32768-token, k = 32, B = 64 prefill stays on the query tiles
     p32k = prob(total_q=32768, total_k=32768, max_seqlen_q=32768, max_seqlen_k=32768, num_heads=32, num_kv_heads=8,
                 top_k=32)
-    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k)) == \
-        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p32k))
-    # the same with k = 16: a staged block serves about 4 queries of a tile, so the block-centric schedule runs
     p32k16 = prob(total_q=32768, total_k=32768, max_seqlen_q=32768, max_seqlen_k=32768, num_heads=32, num_kv_heads=8,
                   top_k=16)
-    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k16)) == \
-        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(p32k16))
+    for pp in (long_ctx, p32k, p32k16):
+        assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(pp)) == both(pp)
+    # a 16384-token prefill with k = 64 has no position where the block-centric schedule wins (E <= 256 < 585)
+    p16k = prob(total_q=16384, total_k=16384, max_seqlen_q=16384, max_seqlen_k=16384, num_heads=32, num_kv_heads=8,
+                top_k=64)
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p16k)) == \
+        lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p16k))
     # decode needs max_seqlen_q == 1
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_DECODE, ctypes.byref(p)) == msa.SIZE_MAX
     d = prob(num_seqs=1, total_q=1, max_seqlen_q=1)
@@ -274,11 +279,12 @@ def test_wait_word_offsets(lib):
     need = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
     off = msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, p)
     assert off == need - 256 + 4 and off % 4 == 0
-    # the automatic call on the tiles has the same word; on the block-centric schedule it has none
+    # the automatic call has the same word: its query-tile part's workspace comes first
     assert msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL, p) == off
     long_ctx = prob(total_q=131072, total_k=131072, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,
                     num_kv_heads=8, block_size=128, top_k=16)
-    assert msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL, long_ctx) is None
+    assert msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL, long_ctx) == \
+        msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, long_ctx)
     for op in (msa.MSA_OP_INDEX_TOPK, msa.MSA_OP_SPARSE_ATTN_DECODE, msa.MSA_OP_SPARSE_ATTN_BACKWARD,
                msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, 99):
         assert msa.msa_workspace_wait_word(op, p) is None
@@ -361,8 +367,11 @@ def test_workspaces_stay_under_the_cap(lib, monkeypatch):
     # 44 GB in one piece
     rag = prob(num_seqs=4, total_q=217091, total_k=217091, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,
                num_kv_heads=8, block_size=128, top_k=16)
-    for op in (msa.MSA_OP_INDEX_TOPK, msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, msa.MSA_OP_SPARSE_ATTN_PREFILL):
+    for op in (msa.MSA_OP_INDEX_TOPK, msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS):
         assert 0 < lib.msa_workspace_size(op, ctypes.byref(rag)) <= CAP
+    # the automatic prefill adds the query tiles' copy of V for its early rows
+    vcopy = 217091 * 8 * 128 * 2
+    assert 0 < lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(rag)) <= CAP + vcopy + (1 << 20)
     # small problems are not split: the index workspace is every row's block scores
     p32k = prob(total_q=32768, total_k=32768, max_seqlen_q=32768, max_seqlen_k=32768, num_heads=32, num_kv_heads=8,
                 top_k=32)
