@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -193,6 +194,113 @@ def measured_traffic(kernels, workload):
             return None
         total += hit[0]["bytes_per_dispatch"]
     return total
+
+
+CALIBRATION_COPIES = 3   # 1 GiB device-to-device copies that --calibrate-copy runs first
+
+
+def _kernel_symbol(name):
+    """Kernel symbol and instance from a profiler kernel name, e.g.
+    'void msa::(anonymous namespace)::attn_prefill_tile<128, 16>(...)' -> ('attn_prefill_tile',
+    'attn_prefill_tile<128, 16>')."""
+    n = name.replace("(anonymous namespace)", "anon")
+    n = n.split("(", 1)[0].strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):   # the last '::' outside template brackets starts the instance
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == ":" and depth == 0 and n[i:i + 2] == "::":
+            cut = i + 2
+    inst = n[cut:] if cut < len(n) else n
+    return inst.split("<", 1)[0], inst
+
+
+def _counter_rows(run_dir, counter):
+    """(dispatch id, kernel name, value) of one rocprofv3 --pmc pass (its *counter_collection.csv),
+    in dispatch order."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (fn, int(row.get("Dispatch_Id") or row.get("Correlation_Id")))
+                name, v = row["Kernel_Name"], float(row["Counter_Value"])
+                per[key] = (name, per[key][1] + v if key in per else v)   # summed over XCDs/instances
+    return [(key[1], name, v) for key, (name, v) in sorted(per.items())]
+
+
+def traffic_table(specs, copy_bytes=1 << 30):
+    """Write profiles/hbm_traffic.json from rocprofv3 counter passes.
+
+    Each spec is WORKLOAD:FETCH_DIR:WRITE_DIR, two passes of `bench.py --workloads WORKLOAD
+    --calibrate-copy` (FETCH_SIZE, then WRITE_SIZE).  The plain device copy of `copy_bytes` that
+    --calibrate-copy runs gives the scale of each counter (bytes per counted KiB); every kernel of
+    the library gets the mean of its dispatches in that pass, scaled, with the SHA-256 of the source
+    file that defines it, so that a later change of the source invalidates the entry."""
+    import hashlib
+    csrc = os.path.join(ROOT, "block_sparse_gqa_amd", "csrc")
+    sources = {}
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith(".hip"):
+            with open(os.path.join(csrc, fn), "rb") as f:
+                sources[fn] = f.read()
+
+    def source_of(symbol):
+        pat = re.compile(rb"__global__[^;{]*?\b" + re.escape(symbol.encode()) + rb"\s*\(", re.S)
+        hits = [fn for fn, text in sources.items() if pat.search(text)]
+        return hits[0] if len(hits) == 1 else None
+
+    def scaled(rows):
+        # the first copies of the run are --calibrate-copy's (the later ones are the ceiling's 4 GiB)
+        copies = [v for _, name, v in rows if "copy" in name.lower()][:CALIBRATION_COPIES]
+        if len(copies) < CALIBRATION_COPIES:
+            raise SystemExit("no calibration copies in the pass: run it with --calibrate-copy")
+        scale = copy_bytes / (float(np.median(copies)) * 1024.0)   # HBM bytes per counted byte
+        kib = {}
+        for _, name, v in rows:
+            kib.setdefault(name, []).append(v)
+        return scale, {name: float(np.mean(v)) for name, v in kib.items()}
+
+    entries = []
+    for spec in specs:
+        workload, fetch_dir, write_dir = spec.split(":")
+        fscale, fetch = scaled(_counter_rows(fetch_dir, "FETCH_SIZE"))
+        wscale, write = scaled(_counter_rows(write_dir, "WRITE_SIZE"))
+        for name in sorted(set(fetch) & set(write)):
+            symbol, inst = _kernel_symbol(name)
+            src = source_of(symbol)
+            if src is None:
+                continue   # not a kernel of this library (the copy, torch's fills)
+            entries.append({
+                "symbol": symbol, "instance": inst, "workload": workload,
+                "source": "block_sparse_gqa_amd/csrc/" + src,
+                "source_sha256": hashlib.sha256(sources[src]).hexdigest(),
+                "fetch_size_kib": fetch[name], "write_size_kib": write[name],
+                "fetch_scale": fscale, "write_scale": wscale,
+                "bytes_per_dispatch": fetch[name] * 1024.0 * fscale + write[name] * 1024.0 * wscale})
+    out = {"note": "HBM bytes per dispatch: FETCH_SIZE and WRITE_SIZE (KiB, mean over the pass's dispatches) "
+                   "times bytes per counted KiB of a plain 1 GiB device copy in the same pass",
+           "kernels": entries}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print("| workload | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |")
+    print("|---|---|---|---|---|---|")
+    for e in entries:
+        print(f"| {e['workload']} | `{e['instance']}` | {e['fetch_size_kib']:,.1f} | {e['write_size_kib']:,.1f} | "
+              f"{e['fetch_size_kib'] * 1024 * e['fetch_scale'] / 1e6:,.1f} | "
+              f"{e['write_size_kib'] * 1024 * e['write_scale'] / 1e6:,.1f} |")
+    log(f"[bench] wrote {path}: {len(entries)} kernels")
 
 
 def decode_reps(dp, bufs, reps=100, flush_mb=1024):
@@ -445,7 +553,13 @@ def main():
                     help="skip timing the other three configurations (reported beside the headline, not in it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--traffic-table", nargs="+", metavar="WORKLOAD:FETCH_DIR:WRITE_DIR",
+                    help="no GPU work: write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                         "passes of `--workloads WORKLOAD --calibrate-copy` runs, and print the table")
     args = ap.parse_args()
+    if args.traffic_table:
+        traffic_table(args.traffic_table)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding of this path is "
               "described in DESIGN.md but not built.", file=sys.stderr)
@@ -460,7 +574,7 @@ def main():
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
-        for _ in range(3):
+        for _ in range(CALIBRATION_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst

@@ -49,25 +49,37 @@ __device__ __forceinline__ RowInfo row_info(long pair, const int32_t *cu_q, cons
 }
 
 // ---------------------------------------------------------------- one wave
+// Grid (rows / 4, h): each wave owns one (row, group) of the rows
+// [row0, row0 + rows); its row and sequence are wave-uniform (scalar).
 template <int VPT>
 __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict__ scores, int e_stride,
                                                         const int32_t *__restrict__ cu_q,
                                                         const int32_t *__restrict__ cu_k, int num_seqs, int row0,
-                                                        int rows, int h, int B, int k, int sink, int local,
+                                                        int rows, int b_shift, int k, int sink, int local,
                                                         int32_t *__restrict__ ids) {
-    // (row, group) pairs of the rows [row0, row0 + rows); scores holds those rows
-    const long pr = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pr >= (long)rows * h) return;   // uniform per wave
-    const long pair = (long)row0 * h + pr;
-    const int t = threadIdx.x & 63;
-    const RowInfo ri = row_info(pair, cu_q, cu_k, num_seqs, h, B);
-    const int E = ri.E;
-    int32_t *out = ids + pair * k;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int r = (int)blockIdx.x * 4 + w;   // row within the chunk (scores holds the chunk's rows)
+    if (r >= rows) return;
+    const int g = (int)blockIdx.y, h = (int)gridDim.y;
+    const int row = row0 + r;
+    int s = 0;
+    if (num_seqs > 1) {
+        int lo = 0, hi = num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+        }
+        s = lo;
+    }
+    const int q0 = cu_q[s];
+    const int p = (cu_k[s + 1] - cu_k[s]) - (cu_q[s + 1] - q0) + (row - q0);
+    const int E = (p >> b_shift) + 1;
+    int32_t *out = ids + ((long)row * h + g) * k;
     if (E <= k) {
-        for (int x = t; x < k; x += 64) out[x] = x < E ? x : -1;
+        for (int x = threadIdx.x & 63; x < k; x += 64) out[x] = x < E ? x : -1;
         return;
     }
-    wave_topk_row<VPT>(scores + pr * e_stride, E, k, sink, local, out);
+    wave_topk_row_fit<VPT>(scores + ((long)r * h + g) * e_stride, E, k, sink, local, out);
 }
 
 // ---------------------------------------------------------------- workgroup
@@ -222,10 +234,10 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
 
 template <int VPT>
 hipError_t launch_wave(const Shape &s, const float *scores, int32_t *ids, hipStream_t st) {
-    const long pairs = (long)s.rows * s.h;
-    hipLaunchKernelGGL((topk_select_wave<VPT>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, scores,
-                       score_stride(s), s.cu_q, s.cu_k, s.num_seqs, s.row0, s.rows, s.h, s.B, s.top_k, s.sink,
-                       s.local, ids);
+    if (s.B < 1 || (s.B & (s.B - 1)) != 0 || s.h > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((topk_select_wave<VPT>), dim3((unsigned)((s.rows + 3) / 4), (unsigned)s.h), dim3(256), 0, st,
+                       scores, score_stride(s), s.cu_q, s.cu_k, s.num_seqs, s.row0, s.rows, __builtin_ctz(s.B),
+                       s.top_k, s.sink, s.local, ids);
     return hipGetLastError();
 }
 
