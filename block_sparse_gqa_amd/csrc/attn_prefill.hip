@@ -32,8 +32,8 @@
 //                     B = Q^T resident in registers;
 //   O^T += V^T . P^T  v_mfma_f32_16x16x32_f16, A = V^T read with the
 //                     transposing ds_read_b64_tr_b16 from an fp16 copy of V
-//                     scaled by one power of two, B = P^T (fp16) straight from
-//                     the S^T accumulators.
+//                     scaled by one power of two per (sequence, KV head),
+//                     B = P^T (fp16) straight from the S^T accumulators.
 // Workgroups are numbered group-fastest, so with 8 groups all tiles of a
 // group run on the same XCD and share its L2.
 #include <algorithm>
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
     const float lt = sum_xor32(sum_xor16(l));
     if (prow < 0) return;
     const int row = q_begin + r0 + qidx;
-    const float inv = lt > 0.f ? __builtin_ldexpf(1.0f / lt, *v_exp) : 0.0f;
+    const float inv = lt > 0.f ? __builtin_ldexpf(1.0f / lt, v_exp[s * h + g]) : 0.0f;
     uint16_t *dst = out + ((size_t)row * H + g * G + head) * D + 4 * q4;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -577,77 +577,172 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
             lt > 0.f ? (m_ref - kPScale + log2f(lt)) * 0.69314718055994531f : -INFINITY;
 }
 
-// fp16 copy of V for the P.V products.  Every value is scaled by the same
-// power of two 2^-e, chosen from max |V| so that the largest lands in
-// [2^14, 2^15): bf16 values within 2^25 of the largest convert exactly, and
-// smaller ones lose only bits below 2^-10 of the largest.  The output is
-// multiplied back by 2^e.
-constexpr int kCvtParts = 1024;   // workgroups of the max pass
+// fp16 copy of V for the P.V products.  The values of one (sequence, KV
+// head) are scaled by one power of two 2^-e, chosen from that head's max |V|
+// in that sequence so that its largest lands in [2^14, 2^15): bf16 values
+// within 2^25 of the largest convert exactly, and smaller ones lose only bits
+// below 2^-10 of the largest.  A tile's output is multiplied back by the 2^e
+// of its own (sequence, group), so a head whose values sit far below those of
+// another keeps its full relative precision.
+//
+// Three passes.  The max and conversion passes run on the grid (sequence,
+// token chunk): chunk c of sequence s covers its tokens [c*T, c*T + T) with
+// all their heads, a contiguous run of V of about 64 KB; chunks past a
+// sequence's end exit at once.  Thread i of a workgroup takes the run's
+// 16-byte pieces i, i + 256, ...; the head of a piece is tracked by adding
+// 256 mod (h*D/8) to its offset within the token row, so no piece costs a
+// division.  Between them one workgroup per (sequence, head) turns the chunk
+// maxima into the exponent.
+constexpr int kCvtChunks = 8192;   // at most this many chunks per sequence
 
-__global__ __launch_bounds__(256) void v_absmax_bits(const uint4 *__restrict__ v, long n16,
-                                                     uint32_t *__restrict__ part) {
-    uint32_t m = 0;
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256) {
-        const uint4 x = v[i];
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
-    }
+struct CvtGrid {
+    int chunks, tokens;   // chunks per sequence, tokens per chunk
+};
+CvtGrid cvt_grid(const Shape &s) {
+    const int mk = std::max(s.max_k, 1);
+    const int rw = std::max(s.h * (s.d / 8), 1);   // pieces per token row
+    int tokens = std::max(1, 4096 / rw);
+    tokens = std::max(tokens, (mk + kCvtChunks - 1) / kCvtChunks);
+    return CvtGrid{(mk + tokens - 1) / tokens, tokens};
+}
+
+__device__ __forceinline__ uint32_t absmax_bf16x8(uint4 x) {
     // |bf16| bit patterns order like the values (NaN above infinity)
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+    return m;
+}
+
+// Max |v| per head over one token chunk of one sequence, as a bf16 bit
+// pattern without the sign, into part[(s * chunks + c) * h + g] (h <= 1024).
+template <int D>
+__global__ __launch_bounds__(256) void v_absmax_bits(const uint4 *__restrict__ v, const int32_t *__restrict__ cu_k,
+                                                     int h, int tokens, int chunks, int kcap,
+                                                     uint32_t *__restrict__ part) {
+    constexpr int CPR = D / 8, SH = D == 128 ? 4 : 3;   // pieces per (token, head), log2
+    __shared__ uint32_t hm[1024];
+    const int s = (int)blockIdx.x, c = (int)blockIdx.y;
+    const int t0 = cu_k[s] + c * tokens;
+    const int t1 = min(cu_k[s] + min(cu_k[s + 1] - cu_k[s], kcap), t0 + tokens);
+    if (t0 >= t1) return;
+    const int rw = h * CPR, step = 256 % rw;
+    for (int g = threadIdx.x; g < h; g += 256) hm[g] = 0u;
+    __syncthreads();
+    const uint4 *run = v + (size_t)t0 * rw;
+    const int n = (t1 - t0) * rw;
+    int r = threadIdx.x % rw, cur = r >> SH;
+    uint32_t m = 0;
+    for (int e0 = threadIdx.x; e0 < n; e0 += 4 * 256) {   // four loads in flight per thread
+        uint4 x[4];
+        int gu[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            x[u] = run[min(e0 + 256 * u, n - 1)];
+            gu[u] = r >> SH;
+            r += step;
+            if (r >= rw) r -= rw;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (e0 + 256 * u >= n) break;
+            if (gu[u] != cur) {
+                atomicMax(&hm[cur], m);
+                cur = gu[u];
+                m = 0;
+            }
+            m = max(m, absmax_bf16x8(x[u]));
+        }
+    }
+    if (threadIdx.x < n) atomicMax(&hm[cur], m);
+    __syncthreads();
+    for (int g = threadIdx.x; g < h; g += 256) part[((size_t)s * chunks + c) * h + g] = hm[g];
+}
+
+// One workgroup per (sequence, head): e[s * h + g] from the maxima of the
+// chunks that hold tokens.  max |v| < 2^(E - 126) for bf16 exponent field E:
+// scaling by 2^-(E - 141) puts it in [2^14, 2^15) whatever its magnitude
+// (2^-e stays a normal float).  Infinities and NaN keep e = 0 and pass
+// through as such.  Workgroup 0 also clears the wait word.
+__global__ __launch_bounds__(256) void v_scale_exp(const int32_t *__restrict__ cu_k, int h, int tokens, int chunks,
+                                                   int kcap, const uint32_t *__restrict__ part,
+                                                   int *__restrict__ v_exp, unsigned *__restrict__ wait_flag) {
+    const int sg = (int)blockIdx.x, s = sg / h, g = sg % h;
+    if (sg == 0 && threadIdx.x == 0) *wait_flag = 0u;   // the attention kernel that follows counts its given-up waits here
+    const int nc = (min(cu_k[s + 1] - cu_k[s], kcap) + tokens - 1) / tokens;
+    uint32_t m = 0;
+#pragma unroll 4
+    for (int c = threadIdx.x; c < nc; c += 256) m = max(m, part[((size_t)s * chunks + c) * h + g]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
     __shared__ uint32_t red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) part[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (threadIdx.x == 0) {
+        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        v_exp[sg] = (m >= 0x7f80u) ? 0 : max(-126, (int)(m >> 7) - 141);
+    }
 }
 
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float mul) {
     return pack_f16x2(__uint_as_float(w << 16) * mul, __uint_as_float(w & 0xffff0000u) * mul);
 }
 
-__global__ __launch_bounds__(256) void v_to_f16(const uint4 *__restrict__ v, long n16,
-                                                const uint32_t *__restrict__ part, int nparts,
-                                                uint4 *__restrict__ v16, int *__restrict__ v_exp,
-                                                unsigned *__restrict__ wait_flag) {
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, part[i]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    __shared__ uint32_t red[4];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+// The fp16 copy of one token chunk of one sequence, each head times its 2^-e.
+// Only the first kcap tokens of each sequence are converted (and measured by
+// the max pass): when the call's rows are split between the schedules, the
+// query tiles stage no key block past the one holding the split position plus
+// one tile.
+template <int D>
+__global__ __launch_bounds__(256) void v_to_f16(const uint4 *__restrict__ v, const int32_t *__restrict__ cu_k, int h,
+                                                int tokens, int kcap, const int *__restrict__ v_exp,
+                                                uint4 *__restrict__ v16) {
+    constexpr int CPR = D / 8, SH = D == 128 ? 4 : 3;
+    const int s = (int)blockIdx.x, c = (int)blockIdx.y;
+    const int t0 = cu_k[s] + c * tokens;
+    const int t1 = min(cu_k[s] + min(cu_k[s + 1] - cu_k[s], kcap), t0 + tokens);
+    if (t0 >= t1) return;
+    __shared__ float muls[1024];
+    const int rw = h * CPR, step = 256 % rw;
+    for (int g = threadIdx.x; g < h; g += 256) muls[g] = __builtin_ldexpf(1.0f, -v_exp[(size_t)s * h + g]);
     __syncthreads();
-    m = max(max(red[0], red[1]), max(red[2], red[3]));
-    // max |v| < 2^(E - 126) for bf16 exponent field E: scaling by 2^-(E - 141)
-    // puts it in [2^14, 2^15) whatever its magnitude (2^-e stays a normal
-    // float).  Infinities and NaN keep e = 0 and pass through as such.
-    const int e = (m >= 0x7f80u) ? 0 : max(-126, (int)(m >> 7) - 141);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *v_exp = e;
-        *wait_flag = 0u;   // the attention kernel that follows counts its given-up waits here
-    }
-    const float mul = __builtin_ldexpf(1.0f, -e);
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256) {
-        const uint4 x = v[i];
-        v16[i] = uint4{bf16x2_to_f16x2(x.x, mul), bf16x2_to_f16x2(x.y, mul), bf16x2_to_f16x2(x.z, mul),
-                       bf16x2_to_f16x2(x.w, mul)};
+    const size_t off = (size_t)t0 * rw;
+    const int n = (t1 - t0) * rw;
+    int r = threadIdx.x % rw;
+    for (int e0 = threadIdx.x; e0 < n; e0 += 4 * 256) {   // four loads in flight per thread
+        uint4 x[4];
+        float mu[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            x[u] = v[off + min(e0 + 256 * u, n - 1)];
+            mu[u] = muls[r >> SH];
+            r += step;
+            if (r >= rw) r -= rw;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (e0 + 256 * u < n)
+                v16[off + e0 + 256 * u] = uint4{bf16x2_to_f16x2(x[u].x, mu[u]), bf16x2_to_f16x2(x[u].y, mu[u]),
+                                                bf16x2_to_f16x2(x[u].z, mu[u]), bf16x2_to_f16x2(x[u].w, mu[u])};
     }
 }
 
-// Workspace: the fp16 copy of V, the max pass's partial maxima, then one
-// 256-byte slot holding the scale exponent (word 0) and the wait word
-// (word 1, the count of ring waits that reached their bound in the last call).
+// Workspace: the fp16 copy of V, the max pass's chunk maxima, the exponents
+// per (sequence, head), then one 256-byte slot whose word 0 is the wait word
+// (the count of ring waits that reached their bound in the last call).
 struct PrefillWs {
     size_t v16_off, part_off, exp_off, flag_off, bytes;
 };
 PrefillWs prefill_ws(const Shape &s) {
     PrefillWs w;
     const size_t vb = (size_t)s.total_k * s.h * s.d * 2;
+    const size_t sh = (size_t)s.num_seqs * s.h;
     w.v16_off = 0;
     w.part_off = (vb + 255) / 256 * 256;
-    w.exp_off = w.part_off + kCvtParts * sizeof(uint32_t);
-    w.flag_off = w.exp_off + sizeof(int);
-    w.bytes = w.exp_off + 256;
+    w.exp_off = w.part_off + ((size_t)s.num_seqs * cvt_grid(s).chunks * s.h * sizeof(uint32_t) + 255) / 256 * 256;
+    w.flag_off = w.exp_off + (sh * sizeof(int) + 255) / 256 * 256;
+    w.bytes = w.flag_off + 256;
     return w;
 }
 
@@ -709,13 +804,30 @@ hipError_t launch_attn_prefill(const Shape &s, const uint16_t *q, const uint16_t
     uint32_t *part = reinterpret_cast<uint32_t *>(wsb + w.part_off);
     int *v_exp = reinterpret_cast<int *>(wsb + w.exp_off);
     unsigned *wait_flag = reinterpret_cast<unsigned *>(wsb + w.flag_off);
-    const long n16 = (long)s.total_k * s.h * s.d / 8;
-    const long need = (n16 + 255) / 256;
-    const int nparts = (int)(need < kCvtParts ? need : kCvtParts);
-    hipLaunchKernelGGL(v_absmax_bits, dim3(nparts), dim3(256), 0, st, reinterpret_cast<const uint4 *>(v), n16, part);
-    const int ncvt = (int)(need < 4096 ? need : 4096);
-    hipLaunchKernelGGL(v_to_f16, dim3(ncvt), dim3(256), 0, st, reinterpret_cast<const uint4 *>(v), n16, part, nparts,
-                       reinterpret_cast<uint4 *>(v16), v_exp, wait_flag);
+    const CvtGrid cg = cvt_grid(s);
+    if (s.h > 1024 || (long)s.num_seqs * s.h > 0x7fffffffL) return hipErrorInvalidValue;
+    // keys the query tiles stage: whole key blocks up to the block holding the
+    // last position they attend (below tiles_below plus one tile).  Masked
+    // keys of a staged block still enter the P.V products with weight 0, so
+    // they must hold converted (finite) values too.
+    const long kc = ((long)s.tiles_below + prefill_tile_queries(s) + s.B - 1) / s.B * s.B;
+    const int kcap = (int)std::min<long>(std::max<long>(kc, 0), 0x7fffffffL);
+    const dim3 cvt((unsigned)s.num_seqs, (unsigned)cg.chunks);
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(v);
+    if (s.d == 64)
+        hipLaunchKernelGGL(v_absmax_bits<64>, cvt, dim3(256), 0, st, v4, s.cu_k, s.h, cg.tokens, cg.chunks, kcap,
+                           part);
+    else
+        hipLaunchKernelGGL(v_absmax_bits<128>, cvt, dim3(256), 0, st, v4, s.cu_k, s.h, cg.tokens, cg.chunks, kcap,
+                           part);
+    hipLaunchKernelGGL(v_scale_exp, dim3((unsigned)(s.num_seqs * s.h)), dim3(256), 0, st, s.cu_k, s.h, cg.tokens,
+                       cg.chunks, kcap, part, v_exp, wait_flag);
+    if (s.d == 64)
+        hipLaunchKernelGGL(v_to_f16<64>, cvt, dim3(256), 0, st, v4, s.cu_k, s.h, cg.tokens, kcap, v_exp,
+                           reinterpret_cast<uint4 *>(v16));
+    else
+        hipLaunchKernelGGL(v_to_f16<128>, cvt, dim3(256), 0, st, v4, s.cu_k, s.h, cg.tokens, kcap, v_exp,
+                           reinterpret_cast<uint4 *>(v16));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nw = prefill_tile_queries(s) / (16 / G);

@@ -155,25 +155,25 @@ __device__ __forceinline__ void wave_topk_row(const float *src, int E, int k, in
     // valid keys share the bits above `top`; start there with zeros below.
     const int top = (mx == mn) ? -1 : 31 - __builtin_clz(mx ^ mn);
     uint32_t T = (top < 0) ? mx : (mx & ~((2u << top) - 1u));
-    bool exact = false;
-    for (int bit = top; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
+    uint32_t m = (top < 0) ? 0u : (1u << top);   // the bit under test
+    for (; m != 0u; m >>= 1) {
+        // (readfirstlane keeps the search in scalar registers: the compiler
+        // otherwise carries T and the bit in vector registers)
+        m = __builtin_amdgcn_readfirstlane(m);
+        const uint32_t cand = __builtin_amdgcn_readfirstlane(T | m);
         int c = 0;
 #pragma unroll
         for (int v = 0; v < VPT; ++v) c += __builtin_popcountll(__ballot(key[v] >= cand));
         if (c >= k) {
             T = cand;
-            if (c == k) {
-                // exactly k keys are >= T: they are the selection (the k-th and
-                // (k+1)-th largest keys lie on opposite sides of T, so no tie
-                // crosses it)
-                exact = true;
-                break;
-            }
+            // exactly k keys are >= T: they are the selection (the k-th and
+            // (k+1)-th largest keys lie on opposite sides of T, so no tie
+            // crosses it)
+            if (c == k) break;
         }
     }
     bool take[VPT];
-    if (exact) {
+    if (m != 0u) {   // stopped early: exactly the keys >= T
 #pragma unroll
         for (int v = 0; v < VPT; ++v) take[v] = key[v] >= T;
     } else {

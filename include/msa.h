@@ -177,9 +177,11 @@ msa_status_t msa_sparse_attn_prefill(const msa_problem_t *problem, const msa_bf1
  * blocks they selected and streams each union block through LDS once.
  * Arguments, layouts and errors as for msa_sparse_attn_prefill.
  * workspace: at least msa_workspace_size(MSA_OP_SPARSE_ATTN_PREFILL_TILES)
- * bytes, 16-byte aligned: an fp16 copy of v (every value scaled by one power
- * of two that puts max |v| in [2^14, 2^15), undone on the output) used for
- * the P.V products, plus a few KB, among them the wait word (see
+ * bytes, 16-byte aligned: an fp16 copy of v (the values of each (sequence,
+ * KV head) scaled by one power of two that puts their max |v| in
+ * [2^14, 2^15), undone on that group's output) used for the P.V products,
+ * plus per-(sequence, head) chunk maxima and exponents (a few KB to MB),
+ * among them the wait word (see
  * msa_workspace_wait_word): the waves of a workgroup hand staged K/V
  * sub-blocks to one another through LDS, and each hand-off wait is bounded;
  * a wait that reaches its bound is counted there and the output of that

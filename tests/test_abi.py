@@ -61,12 +61,25 @@ def test_workspace_size(lib):
     p = prob()
     # [total_q, h, round_up(ceil(max_k / B), 4)] float32 block scores
     assert lib.msa_workspace_size(msa.MSA_OP_INDEX_TOPK, ctypes.byref(p)) == 128 * 2 * 4 * 4
-    # fp16 copy of V [total_k, h, d] (256-byte aligned) + 1024 partial maxima + the scale exponent
-    vbytes = p.total_k * p.num_kv_heads * p.head_dim * 2
-    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p)) == \
-        (vbytes + 255) // 256 * 256 + 1024 * 4 + 256
-    # short context, every position before the split (R = Tq k / E >= 7 while E <= 292): the prefill call runs
-    # the query tiles only
+    # fp16 copy of V [total_k, h, d], per-head maxima of token chunks [num_seqs, chunks, h] (chunks of
+    # max(4096 / (h d / 8), ceil(max_k / 8192)) tokens), exponents [num_seqs, h] (each 256-byte aligned),
+    # then the 256-byte slot of the wait word
+    def r256(n):
+        return (n + 255) // 256 * 256
+
+    def tiles_ws(p):
+        rw = p.num_kv_heads * p.head_dim // 8
+        tokens = max(max(1, 4096 // rw), (p.max_seqlen_k + 8191) // 8192)
+        chunks = (p.max_seqlen_k + tokens - 1) // tokens
+        sh = p.num_seqs * p.num_kv_heads
+        return r256(p.total_k * p.num_kv_heads * p.head_dim * 2) + r256(sh * chunks * 4) + r256(sh * 4) + 256
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p)) == tiles_ws(p)
+    assert tiles_ws(p) == 65536 + 256 + 256 + 256   # 128 tokens: one chunk of 128 tokens
+    p_long = prob(num_seqs=3, total_q=3000, total_k=600000, max_seqlen_q=1000, max_seqlen_k=300000)
+    assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p_long)) == tiles_ws(p_long)
+    assert tiles_ws(p_long) == r256(600000 * 512) + r256(3 * 2 * 2344 * 4) + 256 + 256   # 2344 chunks of 128 tokens
+    # short context, every position before the split (R = Tq k / E >= 8 while E <= 32, i.e. positions below
+    # 2048): the prefill call runs the query tiles only
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == \
         lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
 
@@ -275,10 +288,10 @@ def test_block_prefill_rejects(lib):
 
 def test_wait_word_offsets(lib):
     p = prob()
-    # the tile schedule's workspace ends in a 256-byte slot: scale exponent, then the wait word
+    # the tile schedule's workspace ends in a 256-byte slot whose first word is the wait word
     need = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
     off = msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, p)
-    assert off == need - 256 + 4 and off % 4 == 0
+    assert off == need - 256 and off % 4 == 0
     # the automatic call has the same word: its query-tile part's workspace comes first
     assert msa.msa_workspace_wait_word(msa.MSA_OP_SPARSE_ATTN_PREFILL, p) == off
     long_ctx = prob(total_q=131072, total_k=131072, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,

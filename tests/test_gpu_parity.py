@@ -106,8 +106,8 @@ SMALL = [
     ("decode_k_over_E", (1, 1), (200, 3000), 16, 4, 128, 64, 64, 64, False),
     ("chunked_prefill", (100, 37), (300, 400), 8, 4, 128, 64, 64, 3, False),
     ("empty_sequences", (0, 300, 0, 129), (0, 300, 0, 129), 8, 2, 128, 64, 64, 3, True),
-    # long enough for the automatic prefill to split its rows: query tiles for positions below 2304
-    # (R = 64 * 4 / E >= 7), the block-centric schedule after, across two sequences
+    # long enough for the automatic prefill to split its rows: query tiles for positions below 2048
+    # (R = 64 * 4 / E >= 8), the block-centric schedule after, across two sequences
     ("hybrid_split", (6000, 2500), (6000, 2500), 16, 4, 128, 64, 64, 4, True),
     # one query per non-empty sequence, with empty ones before and between: not the decode shape
     # (total_q != num_seqs), so the index call takes the prefill kernel, which skips them
@@ -144,6 +144,66 @@ def test_value_magnitude(log2_scale):
     err = parity.assert_close(out.float().cpu().numpy() / f, ref_out / f, f"{inp.wl.name} attention / 2^s")
     parity.assert_close(lse.cpu().numpy(), ref_lse, f"{inp.wl.name} lse")
     say(f"[{inp.wl.name}] max err of O / 2^s: {err:.3g}")
+
+
+@pytest.mark.timeout(300)
+def test_value_magnitude_per_head():
+    """V of different (sequence, KV head) pairs scaled by very different powers
+    of two (2^20 down to 2^-28, exact in bf16).  Each group's O / 2^s must meet
+    the tolerance against the oracle's O / 2^s on all three prefill calls: the
+    query-tile schedule scales its fp16 copy of V per (sequence, head), so a
+    head far below another keeps its relative precision (one scale for the
+    whole tensor would flush it to zero), and the block-centric schedule
+    scales per block."""
+    from block_sparse_gqa_amd import device
+    H, h = 8, 4
+    inp = synth.custom((500, 300), (500, 300), H, h, 128, 64, 64, 4, seed=23, name="v_per_head_scales")
+    log2 = np.array([[20, -28, 0, 9], [-12, 3, -28, 20]])   # [sequence, KV head]
+    cu = inp.cu_seqlens_k
+    vf = synth.bf16_bits_to_f32(inp.v)
+    for s in range(2):
+        for g in range(h):
+            vf[cu[s]:cu[s + 1], g] *= np.float32(2.0 ** log2[s, g])
+    inp.v[...] = synth.f32_to_bf16_bits(vf)
+    rows = np.arange(inp.wl.total_q, dtype=np.int64)
+    ref_ids, _, _ = oracle.index_topk(inp, rows)
+    ref_out, ref_lse = oracle.sparse_attention(inp, ref_ids, rows)
+    seq = np.searchsorted(inp.cu_seqlens_q, rows, side="right") - 1
+    f = (2.0 ** log2[seq][:, np.arange(H) // (H // h)]).astype(np.float32)[:, :, None]
+    dp = device.upload(inp)
+    ids = torch.from_numpy(ref_ids).to(dp.q.device)
+    for name, fn in (("auto", device.sparse_attention), ("tiles", device.sparse_attention_tiles),
+                     ("blocks", device.sparse_attention_blocks)):
+        out, lse = fn(dp, ids)
+        torch.cuda.synchronize()
+        err = parity.assert_close(out.float().cpu().numpy() / f, ref_out / f, f"{name}: attention / 2^s")
+        parity.assert_close(lse.cpu().numpy(), ref_lse, f"{name}: lse")
+        say(f"[v_per_head_scales] {name}: max err of O / 2^s {err:.3g}")
+
+
+@pytest.mark.timeout(300)
+def test_split_prefill_ignores_stale_workspace():
+    """The automatic prefill splits this call's rows between the schedules, and
+    the query tiles' fp16 copy of V then covers only the key blocks they can
+    stage.  With the workspace filled with NaN bit patterns before the call, no
+    stale value may reach the output (a masked key still enters the P.V
+    product with weight 0, and 0 * NaN is NaN)."""
+    from block_sparse_gqa_amd import device
+    inp = synth.custom((6000, 2500), (6000, 2500), 16, 4, 128, 64, 64, 4, clustered=True, seed=7,
+                       name="stale_workspace")
+    rows = np.unique(np.concatenate([np.arange(0, 8500, 37), np.arange(2200, 2400), np.arange(6000, 6100)]))
+    ref_ids, _, _ = oracle.index_topk(inp, rows)
+    ref_out, ref_lse = oracle.sparse_attention(inp, ref_ids, rows)
+    given = np.zeros((inp.wl.total_q, 4, 4), np.int32)
+    given[:, :, 1:] = -1
+    given[rows] = ref_ids
+    dp = device.upload(inp)
+    dp.ws_attn.fill_(0xFF)   # fp16 0xFFFF is NaN
+    out, lse = device.sparse_attention(dp, torch.from_numpy(given).to(dp.q.device))
+    torch.cuda.synchronize()
+    err = parity.assert_close(out.float().cpu().numpy()[rows], ref_out, "attention after a NaN-filled workspace")
+    parity.assert_close(lse.cpu().numpy()[rows], ref_lse, "lse after a NaN-filled workspace")
+    say(f"[stale_workspace] max err {err:.3g} over {len(rows)} rows")
 
 
 def test_dense_equivalence_through_gpu():
