@@ -55,7 +55,8 @@ int chunk_rows(const Shape &s, size_t fixed, size_t per_row) {
     // list entries are (row - row0) * top_k + slot in an int
     const size_t lim = (size_t)0x7fffffff / (size_t)(s.top_k > 0 ? s.top_k : 1);
     if (r > lim) r = lim;
-    if (r > (size_t)s.total_q) r = (size_t)s.total_q;
+    const size_t rows = s.rows > 0 ? (size_t)s.rows : (size_t)s.total_q;   // the rows the launch covers
+    if (r > rows) r = rows;
     return r < 1 ? 1 : (int)r;
 }
 
@@ -126,11 +127,33 @@ bool prefill_auto_split(const Shape &s, int *split) {
     return *split <= s.max_k - 1;
 }
 
+// The automatic prefill's two parts when it splits the rows at `split`: the
+// query tiles take the rows whose tile starts below it, the block-centric
+// schedule the rest.  With one sequence the latter are the rows from the
+// first tile that starts at or past the split (positions are
+// total_k - total_q + row), so its lists and partials cover only those.
+void prefill_auto_shapes(const Shape &s, int split, Shape *st_tiles, Shape *st_blocks) {
+    *st_tiles = s;
+    *st_blocks = s;
+    st_tiles->tiles_below = split;
+    st_blocks->blocks_from = split;
+    st_blocks->split_tq = msa::prefill_tile_queries(s);
+    if (s.num_seqs == 1) {
+        const long tq = st_blocks->split_tq;
+        const long first = ((long)split - (s.total_k - s.total_q) + tq - 1) / tq * tq;
+        const int r0 = (int)std::min<long>(std::max<long>(first, 0), s.total_q);
+        st_blocks->row0 = r0;
+        st_blocks->rows = s.total_q - r0;
+    }
+}
+
 size_t prefill_auto_ws(const Shape &s) {
     int split = 0;
     const size_t tiles = msa::prefill_workspace_bytes(s);
     if (!prefill_auto_split(s, &split)) return tiles;
-    return al256(tiles) + msa::block_prefill_workspace_bytes(s);
+    Shape st_tiles, st_blocks;
+    prefill_auto_shapes(s, split, &st_tiles, &st_blocks);
+    return al256(tiles) + msa::block_prefill_workspace_bytes(st_blocks);
 }
 
 msa_status_t check_ws(void *ws, size_t have, size_t need) {
@@ -287,19 +310,8 @@ msa_status_t prefill_call(Schedule which, const msa_problem_t *problem, const ms
     if (!hybrid) return launched(msa::launch_attn_prefill(s, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs));
     // rows split by position: the early ones (few eligible blocks) on the
     // query tiles, the late ones on the block-centric schedule
-    Shape st_tiles = s, st_blocks = s;
-    st_tiles.tiles_below = split;
-    st_blocks.blocks_from = split;
-    st_blocks.split_tq = msa::prefill_tile_queries(s);
-    if (p.num_seqs == 1) {
-        // one sequence: its rows before the first tile that starts at or past
-        // the split (positions are total_k - total_q + row) are all the tiles'
-        const long tq = st_blocks.split_tq;
-        const long first = ((long)split - (p.total_k - p.total_q) + tq - 1) / tq * tq;
-        const int r0 = (int)std::min<long>(std::max<long>(first, 0), p.total_q);
-        st_blocks.row0 = r0;
-        st_blocks.rows = p.total_q - r0;
-    }
+    Shape st_tiles, st_blocks;
+    prefill_auto_shapes(s, split, &st_tiles, &st_blocks);
     char *wsb = static_cast<char *>(workspace);
     if (msa::launch_attn_prefill(st_tiles, q, k, v, topk_ids, softmax_scale, out, lse, workspace, hs) != hipSuccess)
         return MSA_ERROR_LAUNCH;

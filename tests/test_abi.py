@@ -83,9 +83,23 @@ def test_workspace_size(lib):
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == \
         lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
 
-    def both(pp):   # the query tiles' workspace (256-byte aligned), then the block-centric one
+    def both(pp):
+        """The query tiles' workspace (256-byte aligned), then the block-centric one for the rows it takes: one
+        sequence's rows from the first query tile (Tq queries) that starts at or past the split position
+        floor(Tq k / R*) B (R* = 8 for B = 64, 10 for B = 128), i.e. the workspace of a problem with just those
+        rows."""
         t = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(pp))
-        return (t + 255) // 256 * 256 + lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(pp))
+        G = pp.num_heads // pp.num_kv_heads
+        qt = 16 // G
+        nw = 16 if 64 // qt >= 16 else (8 if 64 // qt >= 8 else 4)
+        tq = nw * qt
+        split = (tq * pp.top_k // (10 if pp.block_size >= 128 else 8)) * pp.block_size
+        first = -(-(split - (pp.total_k - pp.total_q)) // tq) * tq
+        rows = pp.total_q - min(max(first, 0), pp.total_q)
+        rest = prob(**{f: getattr(pp, f) for f in ("num_heads", "num_kv_heads", "head_dim", "index_dim", "block_size",
+                                                     "top_k", "total_k", "max_seqlen_k")},
+                    total_q=rows, max_seqlen_q=rows)
+        return (t + 255) // 256 * 256 + lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_BLOCKS, ctypes.byref(rest))
 
     # longer contexts split the rows at a position: tiles before it, the block-centric schedule after it
     long_ctx = prob(total_q=131072, total_k=131072, max_seqlen_q=131072, max_seqlen_k=131072, num_heads=48,
@@ -96,6 +110,8 @@ def test_workspace_size(lib):
                   top_k=16)
     for pp in (long_ctx, p32k, p32k16):
         assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(pp)) == both(pp)
+    # at 32K the split is at position 16384: half the rows' partials (4.4 GB), not all of them
+    assert 4.3e9 < lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k)) < 4.6e9
     # a 16384-token prefill with k = 64 has no position where the block-centric schedule wins (E <= 256 < 585)
     p16k = prob(total_q=16384, total_k=16384, max_seqlen_q=16384, max_seqlen_k=16384, num_heads=32, num_kv_heads=8,
                 top_k=64)

@@ -70,3 +70,32 @@ def test_forced_blocks_paged():
     ref_ids, kth, tie = oracle.index_topk(inp, rows, sink=2, local=1)
     rep = parity.compare_ids(oracle, inp, rows, ids_p.cpu().numpy(), ref_ids, kth, tie)
     say(f"[paged_forced] selection {rep}")
+
+
+# Decode rows whose eligible-block counts sit on every key-width boundary of the
+# one-wave select (1, 2, 4, 8, 16 and 32 keys per lane: 64, 128, ..., 2048
+# blocks): one launch holds them all, and each row takes the narrowest width
+# that holds it.
+WIDTH_EDGES = (33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2047, 2048)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("sink,local", [(0, 0), (1, 2)])
+def test_select_width_boundaries(sink, local):
+    from block_sparse_gqa_amd import device
+    rng = np.random.default_rng(5)
+    B, k = 64, 32
+    lens_k = tuple(int((e - 1) * B + 1 + rng.integers(0, B)) for e in WIDTH_EDGES)   # row position p gives E = p / B + 1
+    inp = synth.custom((1,) * len(lens_k), lens_k, 8, 2, 128, 64, B, k, seed=19, name="width_edges")
+    dp = device.upload(inp)
+    ids = device.index_topk_forced(dp, sink, local) if (sink or local) else device.index_topk(dp)
+    out, lse = device.sparse_attention(dp, ids)
+    torch.cuda.synchronize()
+    gids = ids.cpu().numpy()
+    rows = np.arange(inp.wl.total_q, dtype=np.int64)
+    ref_ids, kth, tie = oracle.index_topk(inp, rows, sink=sink, local=local)
+    rep = parity.compare_ids(oracle, inp, rows, gids, ref_ids, kth, tie)
+    ref_out, ref_lse = oracle.sparse_attention(inp, gids, rows)
+    parity.assert_close(out.float().cpu().numpy(), ref_out, "width edges attention")
+    parity.assert_close(lse.cpu().numpy(), ref_lse, "width edges lse")
+    say(f"[width_edges sink={sink} local={local}] selection {rep}")
