@@ -82,13 +82,16 @@ __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
     // CHUNKS is a multiple of 256 for every supported (d_idx, B).
     static_assert(CHUNKS % 256 == 0, "tile chunks must fill whole passes");
     uint4 pre[PASSES];
+    // The sequence's keys from a scalar base; each load's offset is a 32-bit
+    // byte offset (a sequence's K_idx stays far below 4 GB).
+    const char *kseq = reinterpret_cast<const char *>(k_idx + (size_t)k_begin * DI);
     auto gload = [&](int j) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int ci = ps * 256 + tid;
             const int row = ci / CPR, c8 = ci % CPR;
             const int t = min(j * B + row, len_k - 1);
-            pre[ps] = load16(k_idx + (size_t)(k_begin + t) * DI + c8 * 8);
+            pre[ps] = load16(kseq + (unsigned)(t * (2 * DI) + c8 * 16));
         }
     };
     auto lstore = [&](int buf) {
