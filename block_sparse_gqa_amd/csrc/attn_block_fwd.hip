@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, const int32_t *__restrict__ blk_off,
     const int32_t *__restrict__ off, const int32_t *__restrict__ entries, int num_seqs, int H, int h, int nb_max,
-    int top_k, int row0, float c2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_w) {
+    int top_k, FastDiv kdiv, int row0, float c2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_w) {
     constexpr int KS = D / 32;            // 32-wide k steps over d
     constexpr int DT = D / 16;            // 16-wide d tiles
     constexpr int TT = B / 16;            // 16-token tiles of the block
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
         return (t < ntiles && 16 * mt + l16 < rows_used && x < nq) ? entries[e0 + x] : -1;
     };
     auto load_q = [&](uint4 (&qo)[KS], int ent, int hh) {   // row 0 stands in for unused lanes
-        const size_t base = ((size_t)(ent >= 0 ? row0 + ent / top_k : 0) * H + g * G + hh) * D + 8 * q4;
+        const size_t base = ((size_t)(ent >= 0 ? row0 + (int)fastdiv((uint32_t)ent, kdiv) : 0) * H + g * G + hh) * D + 8 * q4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qo[ks] = load16(q + base + 32 * ks);
     };
@@ -169,21 +169,35 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
                 for (int mt = 0; mt < MT; ++mt) sa[mt][tt] = mfma16x16x32(a, as_bf16x8(qc[mt][ks]), sa[mt][tt]);
             }
         }
-        // Visible tokens of this lane's rows: block token index <= lim.
+        // Visible tokens of this lane's rows: block token index <= lim.  The
+        // causal compare is needed only where some row of the tile sees just
+        // part of the block (its diagonal block); unused lanes count as
+        // seeing all of it (their results are never stored).
         float mu[MT], lsum[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int row = ent_cur[mt] >= 0 ? row0 + ent_cur[mt] / top_k : -1;
-            const int lim = row >= 0 ? shift + (row - q_begin) - j * B : -1;
+            const int row = ent_cur[mt] >= 0 ? row0 + (int)fastdiv((uint32_t)ent_cur[mt], kdiv) : -1;
+            const int lim = row >= 0 ? shift + (row - q_begin) - j * B : B - 1;
             float mx = -INFINITY;
+            if (__ballot(lim < B - 1) == 0) {
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
+                for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = 16 * tt + 4 * q4 + i <= lim ? sa[mt][tt][i] * c2 : -INFINITY;
-                    sa[mt][tt][i] = x;
-                    mx = fmaxf(mx, x);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = sa[mt][tt][i] * c2;
+                        sa[mt][tt][i] = x;
+                        mx = fmaxf(mx, x);
+                    }
+            } else {
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = 16 * tt + 4 * q4 + i <= lim ? sa[mt][tt][i] * c2 : -INFINITY;
+                        sa[mt][tt][i] = x;
+                        mx = fmaxf(mx, x);
+                    }
+            }
             mx = max_xor32(max_xor16(mx));
             mu[mt] = mx == -INFINITY ? 0.f : mx;
             float ls = 0.f;
@@ -196,6 +210,12 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
                     ls += pv;
                 }
             lsum[mt] = sum_xor32(sum_xor16(ls));
+            // P / l, so that the product below is the normalised partial
+            const float inv = lsum[mt] > 0.f ? 1.0f / lsum[mt] : 0.f;
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sa[mt][tt][i] *= inv;
         }
 
         f32x4 oa[MT][DT];
@@ -220,20 +240,18 @@ __global__ __launch_bounds__(64 * fwd_waves<B>()) void fwd_block(
                 for (int mt = 0; mt < MT; ++mt) oa[mt][dt] = mfma16x16x32_f16(va, pb[mt], oa[mt][dt]);
             }
         }
-        // O / l (fp16) goes through this wave's LDS tile, 16 rows at a time,
-        // so that every store instruction writes whole partial rows (16 lanes x
-        // 16 bytes per row for d = 128).
+        // O / l (fp16; P was already divided by l) goes through this wave's
+        // LDS tile, 16 rows at a time, so that every store instruction writes
+        // whole partial rows (16 lanes x 16 bytes per row for d = 128).
         char *my = ot[wave];
         constexpr int CPR = D / 8;      // 16-byte chunks per row
         constexpr int RPI = 64 / CPR;   // rows per store instruction
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const float inv = ent_cur[mt] >= 0 ? 1.0f / lsum[mt] : 0.f;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 *reinterpret_cast<uint2 *>(my + l16 * OSTR + (16 * dt + 4 * q4) * 2) =
-                    uint2{pack_f16x2(oa[mt][dt][0] * inv, oa[mt][dt][1] * inv),
-                          pack_f16x2(oa[mt][dt][2] * inv, oa[mt][dt][3] * inv)};
+                    uint2{pack_f16x2(oa[mt][dt][0], oa[mt][dt][1]), pack_f16x2(oa[mt][dt][2], oa[mt][dt][3])};
             wave_lds_sync();
 #pragma unroll
             for (int x = 0; x < 16 / RPI; ++x) {
@@ -352,8 +370,8 @@ hipError_t launch_fwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
     const hipError_t e = launch_block_lists(s, ids, w.lists, base, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_block<D, B>), dim3((unsigned)w.lists.nb_max, s.h), dim3(64 * fwd_waves<B>()), 0, st, q, k, v, s.cu_q,
-                       s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max, s.top_k, s.row0,
-                       scale * kLog2e, part_o, part_w);
+                       s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)w.lists.nb_max, s.top_k,
+                       make_fastdiv((uint32_t)s.top_k), s.row0, scale * kLog2e, part_o, part_w);
     const long pairs = (long)s.rows * s.h;
     hipLaunchKernelGGL((fwd_merge<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, part_o, part_w, ids, s.cu_q,
                        s.cu_k, s.num_seqs, s.row0, pairs, s.H, s.h, s.B, s.top_k, s.blocks_from, s.split_tq, out,

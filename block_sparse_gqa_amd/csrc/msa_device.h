@@ -156,6 +156,26 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Sequence of a packed row: the last s with cu[s] <= row (binary search over
 // the num_seqs + 1 prefix offsets).
+// floor(n / d) for 0 <= n < 2^31 and 1 <= d < 2^31 without a division:
+// with l = ceil(log2 d) and m = ceil(2^(31 + l) / d) (< 2^32),
+// floor(n m / 2^(31 + l)) = floor(n / d), because n m / 2^(31 + l) exceeds
+// n / d by less than n / 2^(31 + l) < 2^-l <= 1/d.  s = l - 1 is the shift
+// after the high half of the 64-bit product (s = -1 marks d = 1).
+struct FastDiv {
+    uint32_t m;
+    int s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    if (d <= 1) return FastDiv{1u, -1};
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const unsigned long long num = 1ull << (31 + l);
+    return FastDiv{(uint32_t)((num + d - 1) / d), l - 1};
+}
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
+    return f.s < 0 ? n : (__umulhi(n, f.m) >> f.s);
+}
+
 __device__ __forceinline__ int seq_of_row(const int32_t *cu, int num_seqs, int row) {
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {
