@@ -157,8 +157,8 @@ def cpu_baseline(inputs, budget_s=24.0, seed=7):
 
 # The kernels one msa_sparse_attn_prefill call launches (source file, kernel), per schedule; the
 # block-centric part runs in one chunk at the benchmarked sizes.
-_TILE_KERNELS = [("attn_prefill.hip", "v_absmax_bits"), ("attn_prefill.hip", "v_to_f16"),
-                 ("attn_prefill.hip", "attn_prefill_tile")]
+_TILE_KERNELS = [("attn_prefill.hip", "v_absmax_bits"), ("attn_prefill.hip", "v_scale_exp"),
+                 ("attn_prefill.hip", "v_to_f16"), ("attn_prefill.hip", "attn_prefill_tile")]
 _BLOCK_KERNELS = [("block_lists.hip", "lists_block_offsets"), ("block_lists.hip", "fill_zero_i32"),
                   ("block_lists.hip", "lists_count_lds"), ("block_lists.hip", "lists_scan"),
                   ("block_lists.hip", "lists_invert"), ("attn_block_fwd.hip", "fwd_block"),

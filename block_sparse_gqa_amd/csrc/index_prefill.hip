@@ -13,7 +13,7 @@
 // column and 16 keys of a 32-key tile, the block max is an in-register max
 // plus one permlane32 swap.  K_idx tiles are double-buffered in LDS; the
 // block scores of 32 consecutive blocks are staged in LDS and written to the
-// [row, group, block] workspace as contiguous 128-byte runs (whole lines).
+// [row, group, block] workspace as whole 128-byte lines, eight lanes per line.
 #include <type_traits>
 
 #include "msa_device.h"
@@ -157,20 +157,33 @@ __global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
 
         if (slot == kStage - 1 || j == nblk - 1) {
             wave_lds_sync();
-            const int c = lane;
-            const int r = r0 + wave * qw + c / h;
-            const int g = c % h;
-            if (c < qw * h && r < len_q && q_begin + r >= row0 && q_begin + r < row1) {
-                const int E = (shift + r) / B + 1;
-                const int j0 = j - slot;
-                const int n = min(kStage, E - j0);
-                float *dst = scores + ((size_t)(q_begin + r - row0) * h + g) * e_stride + j0;
-                const float *src = stage[wave][c];
-                if (n == kStage) {
+            const int j0 = j - slot;
+            // The wave's earliest row has the fewest blocks: if even it holds
+            // all kStage of them, every column's run is one whole 128-byte
+            // line, and each store instruction writes eight such lines (eight
+            // lanes per column), so memory sees whole lines rather than
+            // 16-byte pieces.
+            if ((shift + r0 + wave * qw) / B + 1 >= j0 + kStage) {
 #pragma unroll
-                    for (int x = 0; x < kStage; x += 4)
-                        *reinterpret_cast<float4 *>(dst + x) = make_float4(src[x], src[x + 1], src[x + 2], src[x + 3]);
-                } else {
+                for (int it = 0; it < kCols / 8; ++it) {
+                    const int c = it * 8 + (lane >> 3), ch = lane & 7;
+                    const int r = r0 + wave * qw + c / h;
+                    const int g = c % h;
+                    if (c < qw * h && r < len_q && q_begin + r >= row0 && q_begin + r < row1) {
+                        const float *src = &stage[wave][c][4 * ch];
+                        *reinterpret_cast<float4 *>(scores + ((size_t)(q_begin + r - row0) * h + g) * e_stride + j0 +
+                                                    4 * ch) = make_float4(src[0], src[1], src[2], src[3]);
+                    }
+                }
+            } else {
+                const int c = lane;
+                const int r = r0 + wave * qw + c / h;
+                const int g = c % h;
+                if (c < qw * h && r < len_q && q_begin + r >= row0 && q_begin + r < row1) {
+                    const int E = (shift + r) / B + 1;
+                    const int n = min(kStage, E - j0);
+                    float *dst = scores + ((size_t)(q_begin + r - row0) * h + g) * e_stride + j0;
+                    const float *src = stage[wave][c];
                     for (int x = 0; x < n; ++x) dst[x] = src[x];
                 }
             }
