@@ -6,7 +6,8 @@
 //    load instruction of a wave reads one contiguous 1 KB run (lane i takes
 //    its i-th 16-byte chunk), eight runs in flight per wave, and consecutive
 //    waves take consecutive runs, which is the access pattern of the decode
-//    index scan.
+//    index scan.  The loads are non-temporal, as the decode kernels' are
+//    (plain loads measured about 9% slower).
 //  * mfma_bf16: back-to-back v_mfma_f32_16x16x32_bf16 on eight independent
 //    accumulators per wave (so no product waits for the previous one), two
 //    waves per SIMD, no memory traffic.
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void stream_read(const uint4 *__restrict__ p, 
         const uint4 *base = p + (i * nwaves + wave) * kChunksPerIter + lane;
         uint4 r[kRuns];
 #pragma unroll
-        for (int u = 0; u < kRuns; ++u) r[u] = base[u * 64];
+        for (int u = 0; u < kRuns; ++u) r[u] = load16_nt(base + u * 64);
 #pragma unroll
         for (int u = 0; u < kRuns; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
     }

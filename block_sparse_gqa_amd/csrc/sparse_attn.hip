@@ -19,6 +19,7 @@
 // Decode splits a sequence's selected blocks over many waves and merges the
 // partial results by log-sum-exp.
 #include <mutex>
+#include <type_traits>
 
 #include "msa.h"
 #include "msa_device.h"
@@ -79,7 +80,7 @@ __device__ __forceinline__ float head_total(float l) {
 // through LDS.  row0 (the cache row of the sub-block's first token) and nvalid
 // (its tokens before the sequence end) are wave-uniform: the base address is
 // scalar and lanes add 32-bit offsets.  Tokens past the end read as zeros.
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void load_kv(uint4 (&kr)[DecodeLds<D>::CH], uint4 (&vr)[DecodeLds<D>::CH],
                                         const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int row0_in,
                                         int nvalid_in, int h, int g) {
@@ -95,11 +96,11 @@ __device__ __forceinline__ void load_kv(uint4 (&kr)[DecodeLds<D>::CH], uint4 (&v
         const int tok = ci / CPR, c16 = ci % CPR;
         const uint32_t off = (uint32_t)(tok * h * D + c16 * 8);
         if (inside) {
-            kr[x] = load16(k + base + off);
-            vr[x] = load16(v + base + off);
+            kr[x] = NT ? load16_nt(k + base + off) : load16(k + base + off);
+            vr[x] = NT ? load16_nt(v + base + off) : load16(v + base + off);
         } else {
-            kr[x] = load16_if(k + base + off, tok < nvalid, k);
-            vr[x] = load16_if(v + base + off, tok < nvalid, v);
+            kr[x] = NT ? load16_nt_if(k + base + off, tok < nvalid, k) : load16_if(k + base + off, tok < nvalid, k);
+            vr[x] = NT ? load16_nt_if(v + base + off, tok < nvalid, v) : load16_if(v + base + off, tok < nvalid, v);
         }
     }
 }
@@ -212,7 +213,7 @@ __device__ __forceinline__ void pv_half(Acc<D> &acc, const f32x4 (&s)[kTT], cons
 // The current sub-block sits in LDS while the next one's loads are in flight.
 // PAGED: k and v are pools of pages of B rows; block j of sequence s sits in
 // page table[s * table_stride + j] (clamped into [0, num_pages)).
-template <int D, int B, bool PAGED>
+template <int D, int B, bool PAGED, bool NT>
 __global__ __launch_bounds__(64, 2) void attn_decode_split(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ ids, const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
@@ -268,10 +269,10 @@ __global__ __launch_bounds__(64, 2) void attn_decode_split(
         }
         wave_lds_sync();
         if (n == 0) continue;
-        load_kv<D>(kA, vA, k, v, rows[0], len_k - list[0], h, g);
-        if (n > 1) load_kv<D>(kB, vB, k, v, rows[1], len_k - list[1], h, g);
+        load_kv<D, NT>(kA, vA, k, v, rows[0], len_k - list[0], h, g);
+        if (n > 1) load_kv<D, NT>(kB, vB, k, v, rows[1], len_k - list[1], h, g);
         store_kv<D>(kA, vA, klds, vlds);
-        if (n > 2) load_kv<D>(kA, vA, k, v, rows[2], len_k - list[2], h, g);
+        if (n > 2) load_kv<D, NT>(kA, vA, k, v, rows[2], len_k - list[2], h, g);
         for (int i = 0; i < n; i += 2) {
             // sub-block i in LDS; set B holds i+1, set A holds i+2
             wave_lds_sync();
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_split(
             wave_lds_sync();
             if (i + 1 >= n) break;
             store_kv<D>(kB, vB, klds, vlds);
-            if (i + 3 < n) load_kv<D>(kB, vB, k, v, rows[i + 3], len_k - list[i + 3], h, g);
+            if (i + 3 < n) load_kv<D, NT>(kB, vB, k, v, rows[i + 3], len_k - list[i + 3], h, g);
             // sub-block i+1 in LDS; set A holds i+2, set B holds i+3
             wave_lds_sync();
             qk_sub<D>(sc, klds, qop);
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_split(
             wave_lds_sync();
             if (i + 2 >= n) break;
             store_kv<D>(kA, vA, klds, vlds);
-            if (i + 4 < n) load_kv<D>(kA, vA, k, v, rows[i + 4], len_k - list[i + 4], h, g);
+            if (i + 4 < n) load_kv<D, NT>(kA, vA, k, v, rows[i + 4], len_k - list[i + 4], h, g);
         }
     }
     const float l = head_total(acc.l);
@@ -364,6 +365,8 @@ __global__ __launch_bounds__(64) void attn_decode_merge(const float *__restrict_
         lse[(size_t)s * H + head] = wsum > 0.f ? (m + log2f(wsum)) * 0.69314718055994531f : -INFINITY;
 }
 
+constexpr double kDecodeStreamBytes = 192.0 * (1 << 20);   // selected K/V per call above which loads are nt
+
 template <int D, int B>
 hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws, hipStream_t st) {
@@ -372,12 +375,23 @@ hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, c
     float *part_o = reinterpret_cast<float *>(ws);
     float *part_lse = part_o + (size_t)s.num_seqs * s.H * nsplit * s.d;
     const dim3 grid(nsplit, s.h, s.num_seqs);
-    if (s.table != nullptr)
-        hipLaunchKernelGGL((attn_decode_split<D, B, true>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.H,
-                           s.h, s.top_k, per, scale * kLog2e, part_o, part_lse, s.table, s.table_stride, s.num_pages);
-    else
-        hipLaunchKernelGGL((attn_decode_split<D, B, false>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.H,
-                           s.h, s.top_k, per, scale * kLog2e, part_o, part_lse, nullptr, 0, 0);
+    // Selections larger than the MALL could keep between calls are streamed
+    // with non-temporal loads (the 4 x 1M decode's 1.07 GB: 196 -> 176 us);
+    // smaller ones keep plain loads, which let consecutive steps find them in
+    // the MALL (the 8 x 64K decode's 134 MB: 31 against 33 us with nt).
+    const double sel_bytes = (double)s.num_seqs * s.h * s.top_k * s.B * s.d * 2.0 * 2.0;
+    const bool nt = sel_bytes > kDecodeStreamBytes;
+    auto go = [&](auto paged, auto ntag) {
+        constexpr bool P = decltype(paged)::value, N = decltype(ntag)::value;
+        hipLaunchKernelGGL((attn_decode_split<D, B, P, N>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.H,
+                           s.h, s.top_k, per, scale * kLog2e, part_o, part_lse, P ? s.table : nullptr,
+                           P ? s.table_stride : 0, P ? s.num_pages : 0);
+    };
+    if (s.table != nullptr) {
+        if (nt) go(std::true_type{}, std::true_type{}); else go(std::true_type{}, std::false_type{});
+    } else {
+        if (nt) go(std::false_type{}, std::true_type{}); else go(std::false_type{}, std::false_type{});
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_decode_merge<D>), dim3(s.H, s.num_seqs), dim3(64), 0, st, part_o, part_lse, s.H, nsplit,

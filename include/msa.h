@@ -377,7 +377,9 @@ msa_status_t msa_index_topk_ex(const msa_problem_t *problem, const msa_select_op
  * the method's kernels are compared with, next to the published peaks.
  *
  * msa_ceiling_stream_read reads the first *bytes_read bytes of `buffer`
- * (device, 16-byte aligned) once with full-line loads and writes nothing but,
+ * (device, 16-byte aligned) once with full-line non-temporal loads (which
+ * stream past L2 and the MALL without settling there, as the decode's K/V
+ * gathers do for large selections) and writes nothing but,
  * in the rarest case, one word of `sink` (device, 4 bytes).  *bytes_read
  * (host) is set before the launch to the largest multiple of the per-launch
  * stride (256 KB per compute unit) that fits in buffer_bytes; a buffer smaller
