@@ -411,13 +411,15 @@ size_t block_prefill_workspace_bytes(const Shape &s) {
 // R = 7 (B = 64) and R = 10 (B = 128).  The rule is applied per query tile:
 // E grows with the position, so the tiles take the early rows and the
 // block-centric schedule the late ones.  Splitting a 32768-token prefill
-// (B = 64, k = 32, G = 4) at 8K, 12K, 16K, 20K and 24K rows took 4.28, 4.35,
-// 4.12, 4.18 and 4.34 ms, against 4.89 ms on the tiles alone; the switch at
-// R = 8 for B = 64 puts that split at 16384.
+// (B = 64, k = 32, G = 4) where R falls below R* = 6, 7, 8, 10 and 12
+// (positions 21824, 18688, 16384, 13056 and 10880) took 4.47, 4.45, 4.40,
+// 4.31 and 4.33 ms, against 4.88 ms on the tiles alone and 5.26 ms on the
+// block-centric schedule alone; on the 217K-token ragged prefill (B = 128)
+// R* = 10, 16 and 24 took 30.8, 30.8 and 31.2 ms.  R* = 10 for both.
 int prefill_split_position(const Shape &s) {
     const int G = s.H / s.h;
     if (G < 1 || G > 16 || s.max_q < 1) return 0x7fffffff;
-    const double thr = s.B >= 128 ? 10.0 : 8.0;
+    const double thr = 10.0;
     // R = Tq k / E < thr  <=>  E > Tq k / thr (with E > k; for E <= k, R = Tq >= 16)
     const long e_star = (long)std::floor((double)prefill_tile_queries(s) * s.top_k / thr) + 1;
     const long p = (e_star - 1) * s.B;

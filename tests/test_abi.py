@@ -78,22 +78,21 @@ def test_workspace_size(lib):
     p_long = prob(num_seqs=3, total_q=3000, total_k=600000, max_seqlen_q=1000, max_seqlen_k=300000)
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p_long)) == tiles_ws(p_long)
     assert tiles_ws(p_long) == r256(600000 * 512) + r256(3 * 2 * 2344 * 4) + 256 + 256   # 2344 chunks of 128 tokens
-    # short context, every position before the split (R = Tq k / E >= 8 while E <= 32, i.e. positions below
-    # 2048): the prefill call runs the query tiles only
+    # short context, every position before the split (R = Tq k / E >= 10 while E <= 25, i.e. positions below
+    # 1600): the prefill call runs the query tiles only
     assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p)) == \
         lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(p))
 
     def both(pp):
         """The query tiles' workspace (256-byte aligned), then the block-centric one for the rows it takes: one
         sequence's rows from the first query tile (Tq queries) that starts at or past the split position
-        floor(Tq k / R*) B (R* = 8 for B = 64, 10 for B = 128), i.e. the workspace of a problem with just those
-        rows."""
+        floor(Tq k / R*) B (R* = 10), i.e. the workspace of a problem with just those rows."""
         t = lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL_TILES, ctypes.byref(pp))
         G = pp.num_heads // pp.num_kv_heads
         qt = 16 // G
         nw = 16 if 64 // qt >= 16 else (8 if 64 // qt >= 8 else 4)
         tq = nw * qt
-        split = (tq * pp.top_k // (10 if pp.block_size >= 128 else 8)) * pp.block_size
+        split = (tq * pp.top_k // 10) * pp.block_size
         first = -(-(split - (pp.total_k - pp.total_q)) // tq) * tq
         rows = pp.total_q - min(max(first, 0), pp.total_q)
         rest = prob(**{f: getattr(pp, f) for f in ("num_heads", "num_kv_heads", "head_dim", "index_dim", "block_size",
@@ -110,8 +109,8 @@ def test_workspace_size(lib):
                   top_k=16)
     for pp in (long_ctx, p32k, p32k16):
         assert lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(pp)) == both(pp)
-    # at 32K the split is at position 16384: half the rows' partials (4.4 GB), not all of them
-    assert 4.3e9 < lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k)) < 4.6e9
+    # at 32K the split is at position 13056: the partials of the 19.7K rows after it (5.3 GB), not all 32K rows'
+    assert 5.1e9 < lib.msa_workspace_size(msa.MSA_OP_SPARSE_ATTN_PREFILL, ctypes.byref(p32k)) < 5.5e9
     # a 16384-token prefill with k = 64 has no position where the block-centric schedule wins (E <= 256 < 585)
     p16k = prob(total_q=16384, total_k=16384, max_seqlen_q=16384, max_seqlen_k=16384, num_heads=32, num_kv_heads=8,
                 top_k=64)

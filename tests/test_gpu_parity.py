@@ -106,8 +106,8 @@ SMALL = [
     ("decode_k_over_E", (1, 1), (200, 3000), 16, 4, 128, 64, 64, 64, False),
     ("chunked_prefill", (100, 37), (300, 400), 8, 4, 128, 64, 64, 3, False),
     ("empty_sequences", (0, 300, 0, 129), (0, 300, 0, 129), 8, 2, 128, 64, 64, 3, True),
-    # long enough for the automatic prefill to split its rows: query tiles for positions below 2048
-    # (R = 64 * 4 / E >= 8), the block-centric schedule after, across two sequences
+    # long enough for the automatic prefill to split its rows: query tiles for positions below 1600
+    # (R = 64 * 4 / E >= 10), the block-centric schedule after, across two sequences
     ("hybrid_split", (6000, 2500), (6000, 2500), 16, 4, 128, 64, 64, 4, True),
     # one query per non-empty sequence, with empty ones before and between: not the decode shape
     # (total_q != num_seqs), so the index call takes the prefill kernel, which skips them
