@@ -27,8 +27,12 @@ constexpr int kWaves = 4;
 constexpr int kCols = 64;     // columns per wave
 constexpr int kStage = 32;    // blocks per staged flush: one 128-byte line of scores per column
 
+// Three workgroups per CU for B = 64 (168 VGPRs, 52 KB of LDS each): with a
+// bound of two the compiler spends 212 VGPRs and only two waves share a SIMD
+// (32K prefill index_topk 0.72 against 0.755 ms).  B = 128 keeps two: its
+// 71 KB of LDS admit no third workgroup.
 template <int DI, int B>
-__global__ __launch_bounds__(256, 2) void index_prefill_blockmax(
+__global__ __launch_bounds__(256, B == 64 ? 3 : 2) void index_prefill_blockmax(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int h,
     float *__restrict__ scores, int e_stride, int row0, int row1) {
