@@ -18,44 +18,6 @@
 
 namespace msa {
 
-// Keys of blocks t*VPT .. t*VPT+VPT-1 (0 past E).  Forced blocks (the first
-// `sink` and the last `local` eligible ones) get the largest key, above that
-// of any score, so they are always kept; the caller guarantees
-// sink + local <= k.
-template <int VPT>
-__device__ __forceinline__ void load_keys(uint32_t (&key)[VPT], const float *src, int t, int E, int sink, int local) {
-#pragma unroll
-    for (int v = 0; v < VPT; v += 4) {
-        const int i = t * VPT + v;
-        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < E) f = *reinterpret_cast<const float4 *>(src + i);
-        const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = i + u;
-            key[v + u] = (j < E) ? ((j < sink || j >= E - local) ? 0xffffffffu : order_key(fv[u])) : 0u;
-        }
-    }
-}
-
-// Wave-level exclusive prefix sum (lane order).
-__device__ __forceinline__ int wave_excl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-    }
-    return incl - x;
-}
-
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
 // Wave-wide max / min of a uint32: DPP permutations inside each row of 16
 // lanes (pair swap, quad swap, half-row mirror, row mirror), then the
 // permlane swaps with the lanes 16 and 32 positions away.  Every lane ends
@@ -90,8 +52,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask, uint32_t acc) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, acc));
 }
 
-// Keys of blocks t*VPT .. t*VPT+VPT-1 of a row of E scores at src, 0 past E
-// (as load_keys).  The loads are unconditional: chunk starts past the row's
+// Keys of blocks t*VPT .. t*VPT+VPT-1 of a row of E scores at src: 0 past E,
+// the largest key for forced blocks (the caller guarantees sink + local <=
+// k).  The loads are unconditional: chunk starts past the row's
 // last chunk are clamped onto it (a cache hit), so no load leaves the row's
 // round_up(E, 4) floats and none waits behind a branch.
 template <int VPT>

@@ -86,26 +86,39 @@ __global__ __launch_bounds__(256) void topk_select_wave(const float *__restrict_
 constexpr int kNT = 1024;
 constexpr int kNW = kNT / 64;
 
-// Block-wide sum; `red` holds kNW ints and is reused after a barrier.
-__device__ __forceinline__ int block_sum(int x, int *red) {
-    x = wave_sum(x);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    int tot = 0;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) tot += red[w];
-    return tot;
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order, without
+// LDS: row_shr steps of 1, 2, 4 and 8 inside each row of 16 lanes (a lane
+// whose source lies outside its row adds 0), then the totals of the lower
+// rows, read from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = (int)(threadIdx.x & 63) >> 4;
+    return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
-// Block-wide exclusive prefix sum in thread order.
-__device__ __forceinline__ int block_excl_scan(int x, int *red) {
-    const int incl = wave_excl_scan(x) + x;
-    __syncthreads();
+// Workgroup-wide exclusive prefix sum in thread order, and the total.  `red`
+// holds kNW ints; callers alternate between two such arrays, so the barrier
+// of one call also separates the reads of the call before it from the
+// writes of the call after it.
+__device__ __forceinline__ int block_excl_scan(int x, int *red, int &total) {
+    const int incl = wave_incl_scan(x);
     if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = incl;
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) base += red[w];
+    const int w = (int)(threadIdx.x >> 6);
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) {
+        const int r = red[i];
+        base += i < w ? r : 0;
+        tot += r;
+    }
+    total = tot;
     return base + incl - x;
 }
 
@@ -116,13 +129,28 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
                                                          int h, int B, int k, int sink, int local,
                                                          int32_t *__restrict__ ids) {
     __shared__ int hist[kBins];
-    __shared__ int red[kNW];
+    __shared__ int red[2][kNW];
+    int nscan = 0;   // scans so far: scan i uses red[i & 1]
     __shared__ uint32_t bc[4];
+    __shared__ uint32_t wmx[kNW], wmn[kNW];
     __shared__ int exact;
 
     const long pr = blockIdx.x;                 // pair within the rows from row0 (scores holds those)
     const long pair = (long)row0 * h + pr;
     const int t = threadIdx.x;
+    // The row's scores are loaded before its length is known (the sequence
+    // search below is a chain of dependent loads): every float4 of the row's
+    // e_stride-float slot is readable, and keys past E are zeroed after.
+    float f[VPT];
+    {
+        const float *src = scores + pr * e_stride;
+#pragma unroll
+        for (int v = 0; v < VPT; v += 4) {
+            const int i = min(t * VPT + v, e_stride - 4);
+            const float4 x = *reinterpret_cast<const float4 *>(src + i);
+            f[v] = x.x; f[v + 1] = x.y; f[v + 2] = x.z; f[v + 3] = x.w;
+        }
+    }
     const RowInfo ri = row_info(pair, cu_q, cu_k, num_seqs, h, B);
     const int E = ri.E;
     int32_t *out = ids + pair * k;
@@ -131,32 +159,30 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
         return;
     }
     uint32_t key[VPT];
-    load_keys<VPT>(key, scores + pr * e_stride, t, E, sink, local);
-
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int j = t * VPT + v;
+        key[v] = j < E ? ((j < sink || j >= E - local) ? 0xffffffffu : order_key(f[v])) : 0u;
+    }
     uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         mx = max(mx, key[v]);
         mn = min(mn, key[v] ? key[v] : 0xffffffffu);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-    }
-    if (t == 0) {
-        bc[0] = 0u;
-        bc[1] = 0xffffffffu;
-        exact = 0;
-    }
-    __syncthreads();
+    mx = wave_max_u32(mx);
+    mn = wave_min_u32(mn);
     if ((t & 63) == 0) {
-        atomicMax(&bc[0], mx);
-        atomicMin(&bc[1], mn);
+        wmx[t >> 6] = mx;
+        wmn[t >> 6] = mn;
     }
+    if (t == 0) exact = 0;
     __syncthreads();
-    mx = bc[0];
-    mn = bc[1];
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) {
+        mx = max(mx, wmx[i]);
+        mn = min(mn, wmn[i]);
+    }
 
     // Radix select of the k-th largest key below the common prefix.
     uint32_t T;
@@ -180,7 +206,8 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
             const int nb = 1 << w;
             const int b0 = nb - 1 - 2 * t, b1 = b0 - 1;
             const int c0 = (b0 >= 0) ? hist[b0] : 0, c1 = (b1 >= 0) ? hist[b1] : 0;
-            const int above = block_excl_scan(c0 + c1, red);   // keys in bins above b0
+            int all;
+            const int above = block_excl_scan(c0 + c1, red[nscan++ & 1], all);   // keys in bins above b0
             if (b0 >= 0 && above < rank && above + c0 >= rank) {
                 bc[2] = (uint32_t)b0;
                 bc[3] = (uint32_t)above;
@@ -195,7 +222,9 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
             rank -= (int)bc[3];
             lo_bit = sh;
             const bool done = exact != 0;
-            __syncthreads();
+            // (no barrier here: the next pass clears hist and rewrites bc and
+            // exact only after barriers that every thread reaches after these
+            // reads)
             if (done && P > 0u) {
                 // the k-th largest key is the smallest in its bin: the keys
                 // from that bin up are exactly the selection, no tie crosses it
@@ -212,8 +241,13 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
         n_gt += key[v] > T;
         n_eq += key[v] == T;
     }
-    const int need_eq = k - block_sum(n_gt, red);
-    int eq_seen = block_excl_scan(n_eq, red);
+    // One scan of both counts: keys > T in the low 13 bits (at most k <=
+    // 4096 of them in the whole row, so no carry), keys == T above them (at
+    // most kNT * 64 = 2^16, so the sum stays below 2^29).
+    int both;
+    const int ex = block_excl_scan((n_eq << 13) | n_gt, red[nscan++ & 1], both);
+    const int need_eq = k - (both & 0x1fff);
+    int eq_seen = ex >> 13;
     int sel = 0;
     bool take[VPT];
 #pragma unroll
@@ -226,7 +260,8 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
         take[v] = tk;
         sel += tk;
     }
-    int pos = block_excl_scan(sel, red);
+    int n_sel;
+    int pos = block_excl_scan(sel, red[nscan++ & 1], n_sel);
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
         if (take[v] && pos < k) out[pos++] = t * VPT + v;
