@@ -245,6 +245,38 @@ def test_planted_and_all_ties_closed_forms():
         assert list(g["ids"][row, 0]) == list(range(m)) + [-1] * (K - m)
 
 
+# name, context length, block size, top_k, period of the block-score levels:
+# decode rows long enough for the workgroup-level select, with many exactly
+# equal block scores.
+LONG_TIES = [
+    ("e4096_k1024_all_equal", 4096 * 64, 64, 1024, 1),
+    ("e4096_k2048_three_levels", 4096 * 64, 64, 2048, 3),
+    ("e40000_k4096_seven_levels", 40000 * 64, 64, 4096, 7),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case", LONG_TIES, ids=[c[0] for c in LONG_TIES])
+def test_long_row_ties_closed_forms(case):
+    """Block j's score is exactly 1 + (j mod period): the selection is every
+    block of the top level from the lowest id on, then the next level's
+    lowest ids, i.e. the first k blocks in (score desc, id asc) order."""
+    name, L, B, K, period = case
+    say(f"[{name}] decode at context {L}")
+    inp = synth.custom((1,), (L,), 2, 1, 64, 32, B, K, seed=3, name=name)
+    q_idx = np.zeros((1, 1, 32), np.float32)
+    q_idx[0, 0, 0] = 1.0
+    k_idx = np.zeros((L, 32), np.float32)
+    k_idx[:, 0] = 1.0 + (np.arange(L) // B) % period
+    inp.q_idx = synth.f32_to_bf16_bits(q_idx)
+    inp.k_idx = synth.f32_to_bf16_bits(k_idx)
+    g = run_gpu(inp)
+    E = L // B
+    level = 1 + np.arange(E) % period
+    first_k = np.lexsort((np.arange(E), -level))[:K]
+    assert list(g["ids"][0, 0]) == sorted(int(x) for x in first_k)
+
+
 def test_determinism():
     inp = synth.custom((777,), (777,), 16, 4, 128, 64, 64, 5, seed=5)
     a = run_gpu(inp)
