@@ -194,8 +194,10 @@ __device__ __forceinline__ unsigned long long lds_u64(uint32_t addr) {
     return v;
 }
 
+// (no wait: the wave's later LDS operations are ordered after it anyway, and
+// the waves that poll the word need no more than that it lands)
 __device__ __forceinline__ void lds_store_u32(uint32_t addr, int v) {
-    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 // One wave-level increment of the counter at addr; returns its prior value
 // (the same in every lane).
@@ -505,14 +507,22 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_prefill_tile(
         };
 
         for (int e0 = 0; e0 < count; e0 += 64) {
-            const unsigned long long m_e = (e0 + lane < count) ? lds_u64(list_m0 + 8 * (e0 + lane)) : 0ull;
+            // 64 list entries at a time, one per lane; an item's entry is then
+            // read from its lane (no LDS round trip per item)
+            const bool in_list = e0 + lane < count;
+            const unsigned long long m_e = in_list ? lds_u64(list_m0 + 8 * (e0 + lane)) : 0ull;
+            const int n_e = in_list ? (int)lds_u32(list_n0 + 4 * (e0 + lane)) : 0;
+            const int u_e = in_list ? (int)lds_u32(list_u0 + 4 * (e0 + lane)) : 0;
             unsigned long long act = __ballot((m_e & tile_bits) != 0ull);
             while (act != 0ull) {
-                const int ei = e0 + __builtin_ctzll(act);
+                const int li = __builtin_ctzll(act);
+                const int ei = e0 + li;
                 act &= act - 1ull;
-                const unsigned long long mk = lds_u64(list_m0 + 8 * ei);
-                const int nact = __builtin_amdgcn_readfirstlane((int)lds_u32(list_n0 + 4 * ei));
-                const int blk = __builtin_amdgcn_readfirstlane((int)lds_u32(list_u0 + 4 * ei));
+                const unsigned long long mk =
+                    ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(m_e >> 32), li) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m_e, li);
+                const int nact = __builtin_amdgcn_readlane(n_e, li);
+                const int blk = __builtin_amdgcn_readlane(u_e, li);
                 for (int sub = 0; sub < nsub; ++sub) {
                     const int it = ei * nsub + sub;
                     if (it >= nitems) break;
