@@ -109,6 +109,8 @@ SMALL = [
     # long enough for the automatic prefill to split its rows: query tiles for positions below 1600
     # (R = 64 * 4 / E >= 10), the block-centric schedule after, across two sequences
     ("hybrid_split", (6000, 2500), (6000, 2500), 16, 4, 128, 64, 64, 4, True),
+    # the same split inside chunked prefills (queries at positions 1000..2999 and 1500..2199 of their sequences)
+    ("hybrid_split_chunked", (2000, 700), (3000, 2200), 16, 4, 128, 64, 64, 4, True),
     # one query per non-empty sequence, with empty ones before and between: not the decode shape
     # (total_q != num_seqs), so the index call takes the prefill kernel, which skips them
     ("decode_like_empty_seqs", (0, 1, 0, 1), (50, 700, 300, 1500), 32, 8, 128, 64, 64, 8, False),
