@@ -367,6 +367,9 @@ __global__ __launch_bounds__(64) void attn_decode_merge(const float *__restrict_
 
 constexpr double kDecodeStreamBytes = 192.0 * (1 << 20);   // selected K/V per call above which loads are nt
 
+// K and V bytes a decode call gathers: top_k blocks of each per (sequence, group).
+double decode_selected_bytes(const Shape &s) { return (double)s.num_seqs * s.h * s.top_k * s.B * s.d * 2.0 * 2.0; }
+
 template <int D, int B>
 hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *ids, float scale, uint16_t *out, float *lse, void *ws, hipStream_t st) {
@@ -379,8 +382,7 @@ hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, c
     // with non-temporal loads (the 4 x 1M decode's 1.07 GB: 196 -> 176 us);
     // smaller ones keep plain loads, which let consecutive steps find them in
     // the MALL (the 8 x 64K decode's 134 MB: 31 against 33 us with nt).
-    const double sel_bytes = (double)s.num_seqs * s.h * s.top_k * s.B * s.d * 2.0 * 2.0;
-    const bool nt = sel_bytes > kDecodeStreamBytes;
+    const bool nt = decode_selected_bytes(s) > kDecodeStreamBytes;
     auto go = [&](auto paged, auto ntag) {
         constexpr bool P = decltype(paged)::value, N = decltype(ntag)::value;
         hipLaunchKernelGGL((attn_decode_split<D, B, P, N>), grid, dim3(64), 0, st, q, k, v, ids, s.cu_q, s.cu_k, s.H,
@@ -402,11 +404,14 @@ hipError_t launch_decode(const Shape &s, const uint16_t *q, const uint16_t *k, c
 }  // namespace
 
 int decode_splits(const Shape &s) {
-    // Aim for ~768 waves (three per CU); each split keeps at least one block.
-    // At 1M context a sweep of 512-2048 waves put 768 at 194 us against 208 us
-    // for 2048: each wave then streams longer runs of blocks.
+    // Aim for ~768 waves (three per CU) when the selection streams from HBM,
+    // ~1024 when it is small enough to stay in the MALL; each split keeps at
+    // least one block.  Swept with the current kernels (512, 768, 1024, 1536
+    // waves): the 4 x 1M decode's attention took 200, 175, 188 and 178 us, the
+    // 8 x 64K decode's 32.1, 31.4, 29.9 and 32.2 us.
     long pairs = (long)s.num_seqs * s.h;
-    long want = (768 + pairs - 1) / pairs;
+    const long waves = decode_selected_bytes(s) > kDecodeStreamBytes ? 768 : 1024;
+    long want = (waves + pairs - 1) / pairs;
     if (want > s.top_k) want = s.top_k;
     if (want < 1) want = 1;
     if (want > 256) want = 256;
