@@ -15,6 +15,7 @@ as a bf16 partial, accumulate in float32 and round dq, dk, dv to bf16
 gradient (D from the unrounded output) is printed beside it: it adds the
 effect of out's bf16 rounding on D.
 """
+import dataclasses
 import sys
 import zlib
 
@@ -124,3 +125,34 @@ def test_backward_repeat():
     for x, y, n in ((a[1], b[1], "dk"), (a[2], b[2], "dv")):
         xf, yf = x.float(), y.float()
         assert float((xf - yf).abs().max()) <= 2 ** -7 * float(xf.abs().max()), n
+
+
+@pytest.mark.timeout(600)
+def test_backward_full_size_sampled_rows():
+    """The 32768-token prefill's backward at full size (the measured configuration, run in two row chunks), checked
+    on sampled rows: dq of a row depends only on its own selection, K and V, so the oracle computes it for a
+    contiguous range of rows posed as a prefill of those rows against every key before them."""
+    from block_sparse_gqa_amd import device
+    inp = synth.make_inputs("prefill_32k")
+    wl = inp.wl
+    rng = np.random.default_rng(11)
+    dout_bits = synth.f32_to_bf16_bits(rng.standard_normal(inp.q.shape).astype(np.float32))
+    dp = device.upload(inp)
+    ids, out, lse = device.forward(dp)
+    dout = device.to_device_bf16(dout_bits)
+    say("[bwd_full] gpu backward, 32768 tokens")
+    dq, _, _ = device.sparse_attention_backward(dp, ids, out, lse, dout)
+    torch.cuda.synchronize()
+    gids = ids.cpu().numpy()
+    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    dq_gpu = dq.float().cpu().numpy()
+    del dp, ids, out, lse, dout, dq
+    torch.cuda.empty_cache()
+    n = wl.total_q
+    for a, b in ((0, 192), (13000, 13192), (n - 192, n)):
+        sub_wl = dataclasses.replace(wl, name=f"rows_{a}_{b}", seqlens_q=(b - a,), seqlens_k=(b,))
+        sub = synth.Inputs(sub_wl, np.array([0, b - a], np.int32), np.array([0, b], np.int32), inp.q[a:b],
+                           inp.k[:b], inp.v[:b], inp.q_idx[a:b], inp.k_idx[:b])
+        rq, _, _ = oracle.sparse_attention_backward(sub, gids[a:b], dout_bits[a:b], out=out_bits[a:b])
+        e = check_grad(dq_gpu[a:b], rq, f"bwd_full dq rows {a}..{b}")
+        say(f"[bwd_full] rows {a}..{b}: largest |err| / (2e-3 + 1e-2 |ref|) of dq {e:.3g}")
