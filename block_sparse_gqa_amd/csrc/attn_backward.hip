@@ -11,8 +11,8 @@
 //
 // Key-centric schedule.  dk and dv of a key block need every (query, head)
 // that selected it, so the query-centric ids are first turned into one list
-// of selecting queries per (group, block) (block_lists.hip; list order is not
-// fixed, so dk/dv sums are not bitwise reproducible).  One workgroup then
+// of selecting queries per (group, block) (block_lists.hip; each list is
+// sorted, so the dk/dv sums run in a fixed order).  One workgroup then
 // owns one (group, block): K and V of the block sit in LDS, dk and dv in
 // registers, and the selecting queries stream through in chunks of up to 32
 // (query, head) rows.  For each chunk and 16-token tile:
@@ -479,7 +479,8 @@ hipError_t launch_bwd(const Shape &s, const uint16_t *q, const uint16_t *k, cons
         const int32_t *blk_off = reinterpret_cast<const int32_t *>(base + lists.blk_off);
         const int32_t *off = reinterpret_cast<const int32_t *>(base + lists.off);
         const int32_t *entries = reinterpret_cast<const int32_t *>(base + lists.entries);
-        const hipError_t e = launch_block_lists(c, ids, lists, base, st);
+        // sorted lists: dk and dv then sum in a fixed order, bitwise reproducible
+        const hipError_t e = launch_block_lists(c, ids, lists, base, st, true);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_block<D, B>), dim3((unsigned)lists.nb_max, s.h), dim3(256), 0, st, q, k, v, dout, lse,
                            delta, s.cu_q, s.cu_k, blk_off, off, entries, s.num_seqs, s.H, s.h, (int)lists.nb_max,

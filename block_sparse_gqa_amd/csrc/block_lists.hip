@@ -13,7 +13,9 @@
 // sequences, a count whose atomics also give each selection its place in its
 // list, an exclusive scan of the counts, and a scatter.  The place a
 // selection gets depends on the order the atomics run in, so list order is
-// fixed only per run.
+// fixed only per run, unless the caller asks for a fifth pass that sorts
+// every list ascending (the backward does: its dk and dv sums run in list
+// order).
 #include <algorithm>
 
 #include "msa_device.h"
@@ -168,6 +170,43 @@ __global__ __launch_bounds__(kScanThreads) void lists_scan(const int32_t *__rest
     if (threadIdx.x == 0) off[n] = carry;
 }
 
+// Sorts each key's entries ascending (bitonic, in LDS), so that a kernel
+// walking a list sees its entries in one fixed order whatever order the
+// atomics of the count pass handed out the places in.  One instance per list
+// length class: lists of lo < n <= CAP entries; longer ones are the next
+// instance's, and lists longer than the largest CAP keep their order.
+template <int CAP, int NT>
+__global__ __launch_bounds__(NT) void lists_sort(const int32_t *__restrict__ off, int32_t *__restrict__ entries,
+                                                 int lo) {
+    __shared__ int sbuf[CAP];
+    const long key = blockIdx.x;
+    const int e0 = off[key], n = off[key + 1] - e0;
+    if (n <= lo || n > CAP || n < 2) return;
+    int N = 2;
+    while (N < n) N <<= 1;
+    for (int i = threadIdx.x; i < N; i += NT) sbuf[i] = i < n ? entries[e0 + i] : 0x7fffffff;
+    __syncthreads();
+    for (int kk = 2; kk <= N; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            // pair p compares i (bit j clear) with i + j
+            for (int p = threadIdx.x; p < N / 2; p += NT) {
+                const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+                const int l = i | j;
+                const int a = sbuf[i], b = sbuf[l];
+                if ((a > b) == ((i & kk) == 0)) {
+                    sbuf[i] = b;
+                    sbuf[l] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = threadIdx.x; i < n; i += NT) entries[e0 + i] = sbuf[i];
+}
+
+constexpr int kSortSmall = 2048;   // most lists: 8 KB of LDS, many workgroups per CU
+constexpr int kSortCap = 16384;    // longest list sorted (64 KB of LDS)
+
 __global__ __launch_bounds__(256) void fill_zero_i32(int32_t *__restrict__ p, long n) {
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0;
 }
@@ -194,7 +233,8 @@ BlockLists block_lists_layout(const Shape &s) {
     return w;
 }
 
-hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLists &w, char *base, hipStream_t st) {
+hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLists &w, char *base, hipStream_t st,
+                              bool sorted) {
     int32_t *blk_off = reinterpret_cast<int32_t *>(base + w.blk_off);
     int32_t *cnt = reinterpret_cast<int32_t *>(base + w.cnt);
     int32_t *off = reinterpret_cast<int32_t *>(base + w.off);
@@ -226,6 +266,13 @@ hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLis
         hipLaunchKernelGGL((lists_invert<1>), egrid, dim3(256), 0, st, ids, s.cu_q, s.cu_k, blk_off, s.num_seqs, s.h,
                            s.B, s.top_k, (int)w.nb_max, s.row0, s.blocks_from, s.split_tq, n, cnt, place, off,
                            entries);
+    if (sorted && n > 0) {
+        hipLaunchKernelGGL((lists_sort<kSortSmall, 256>), dim3((unsigned)keys), dim3(256), 0, st, off, entries, 1);
+        // a list holds at most one entry per row of the chunk
+        if (s.rows > kSortSmall)
+            hipLaunchKernelGGL((lists_sort<kSortCap, 1024>), dim3((unsigned)keys), dim3(1024), 0, st, off, entries,
+                               kSortSmall);
+    }
     return hipGetLastError();
 }
 

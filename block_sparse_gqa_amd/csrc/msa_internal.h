@@ -96,7 +96,10 @@ struct BlockLists {
     long nb_max;
 };
 BlockLists block_lists_layout(const Shape &s);
-hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLists &w, char *base, hipStream_t st);
+// sorted: each list in ascending entry order (lists of at most 16384
+// entries; longer ones keep the count pass's order).
+hipError_t launch_block_lists(const Shape &s, const int32_t *ids, const BlockLists &w, char *base, hipStream_t st,
+                              bool sorted = false);
 // Backward of the sparse branch (prefill, selection fixed).
 size_t backward_workspace_bytes(const Shape &s);
 hipError_t launch_attn_backward(const Shape &s, const uint16_t *q, const uint16_t *k, const uint16_t *v,

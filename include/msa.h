@@ -277,9 +277,12 @@ msa_status_t msa_sparse_attn_prefill_blocks(const msa_problem_t *problem, const 
  * bytes, 16-byte aligned: dO.O per row, one bf16 partial of dq per (row,
  * selected slot, head) -- total_q * top_k * H * d * 2 bytes, the bulk of it
  * (8.6 GB for 32K tokens, 32 heads, k = 32) -- and the per-(group, block)
- * lists of selecting queries.  dk/dv sums run in list order, which atomics
- * fix at run time, so they are not bitwise reproducible from call to call
- * (within rounding); dq is.  Needs H/h <= 32 and total_q * top_k < 2^31.
+ * lists of selecting queries.  dk/dv sums run in list order; each list is
+ * sorted first, so dq, dk and dv are bitwise reproducible from call to call
+ * as long as no key block is selected by more than 16384 rows of one row
+ * chunk (longer lists keep the order the count pass's atomics gave them,
+ * and their dk/dv agree only to rounding).  Needs H/h <= 32 and
+ * total_q * top_k < 2^31.
  */
 msa_status_t msa_sparse_attn_prefill_backward(const msa_problem_t *problem, const msa_bf16_t *q,
                                               const msa_bf16_t *k, const msa_bf16_t *v, const int32_t *topk_ids,
