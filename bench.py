@@ -360,21 +360,21 @@ def paged_decode(inp, dp, ids_contig, contig, steps, warmup):
     for _ in range(warmup):
         device.index_topk_paged(dp, pc, ids)
         device.sparse_attention_paged(dp, pc, ids, out, lse)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = timed_events(steps)
     for x in ev:
         x[0].record()
         device.index_topk_paged(dp, pc, ids)
-        x[1].record()
         device.sparse_attention_paged(dp, pc, ids, out, lse)
         x[2].record()
     torch.cuda.synchronize()
-    t_idx = float(np.mean([x[0].elapsed_time(x[1]) for x in ev]))
-    t_att = float(np.mean([x[1].elapsed_time(x[2]) for x in ev]))
-    gbs = contig["algorithmic_GB"] / ((t_idx + t_att) * 1e-3)
+    t_all = float(np.mean([x[0].elapsed_time(x[2]) for x in ev]))
+    t_idx, t_att = split_pass(lambda: device.index_topk_paged(dp, pc, ids),
+                              lambda: device.sparse_attention_paged(dp, pc, ids, out, lse), steps)
+    gbs = contig["algorithmic_GB"] / (t_all * 1e-3)
     same = bool(torch.equal(ids, ids_contig))
     del pc
     torch.cuda.empty_cache()
-    return {"ms": t_idx + t_att, "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "GB_per_s": gbs,
+    return {"ms": t_all, "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "GB_per_s": gbs,
             "frac_hbm_peak": gbs / HBM_PEAK_GBS, "pages": num_pages, "ids_equal_contiguous": same,
             "page_in_ms": t_append, "page_in_GB_per_s": append_bytes / (t_append * 1e-3) / 1e9}
 
@@ -459,25 +459,55 @@ def prefill_schedule_of(dp):
     return "tiles+blocks"
 
 
-def summarize(inp, dp, ids, evs):
-    """Per-workload result from the events of its timed calls: (index start, index end = attention
-    start, attention end) per step.  Returns the result dict and the (name, ms, bound, work, counters)
+def split_pass(index_call, attn_call, steps):
+    """Index and attention times of one workload, from `steps` passes with a marker between the two
+    calls.  Each marker costs the GPU a few microseconds of idle time, so the timed steps carry none
+    between the calls of a workload whose split is not needed live; this pass gives that split
+    instead (its two parts sum to slightly more than the step's own time)."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for x in ev:
+        x[0].record()
+        index_call()
+        x[1].record()
+        attn_call()
+        x[2].record()
+    torch.cuda.synchronize()
+    return (float(np.mean([x[0].elapsed_time(x[1]) for x in ev])),
+            float(np.mean([x[1].elapsed_time(x[2]) for x in ev])))
+
+
+def timed_events(n):
+    """`n` (start, None, end) triples for back-to-back timed passes of one workload."""
+    import torch
+    return [[torch.cuda.Event(enable_timing=True), None, torch.cuda.Event(enable_timing=True)] for _ in range(n)]
+
+
+def summarize(inp, dp, ids, evs, split=None):
+    """Per-workload result from the events of its timed calls: (start, index end = attention start or
+    None, end) per step.  Without the middle marker, `split` gives the index and attention times from a
+    separate pass (split_pass).  Returns the result dict and the (name, ms, bound, work, counters)
     entries of its two calls for the roofline."""
     from block_sparse_gqa_amd import msa
     wl, name = inp.wl, inp.wl.name
-    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     per_step = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    t_all = float(per_step.mean())
+    if evs[0][1] is not None:
+        t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    else:
+        t_idx, t_att = split
     alg = algorithmic(inp, dp, ids)
     kernels = []
-    r = {"tokens": wl.total_q, "ms": t_idx + t_att, "tokens_per_s": wl.total_q / ((t_idx + t_att) * 1e-3),
+    r = {"tokens": wl.total_q, "ms": t_all, "tokens_per_s": wl.total_q / (t_all * 1e-3),
          "ms_median": float(np.median(per_step)), "ms_min": float(per_step.min()),
-         "index_topk_ms": t_idx, "sparse_attn_ms": t_att, "selected_tokens": alg["selected_tokens"],
-         "workload": wl.description}
+         "index_topk_ms": t_idx, "sparse_attn_ms": t_att,
+         "split_timing": "markers in the timed steps" if evs[0][1] is not None else "separate pass",
+         "selected_tokens": alg["selected_tokens"], "workload": wl.description}
     if wl.is_decode:
         gbs_i = alg["index_bytes"] / (t_idx * 1e-3) / 1e9
         gbs_a = alg["attn_bytes"] / (t_att * 1e-3) / 1e9
-        tot = (alg["index_bytes"] + alg["attn_bytes"]) / ((t_idx + t_att) * 1e-3) / 1e9
+        tot = (alg["index_bytes"] + alg["attn_bytes"]) / (t_all * 1e-3) / 1e9
         r.update({"bound": "hbm", "algorithmic_GB": (alg["index_bytes"] + alg["attn_bytes"]) / 1e9,
                   "GB_per_s": tot, "frac_hbm_peak": tot / HBM_PEAK_GBS,
                   "index_topk_GB_per_s": gbs_i, "sparse_attn_GB_per_s": gbs_a})
@@ -486,7 +516,7 @@ def summarize(inp, dp, ids, evs):
     else:
         tf_i = alg["index_flops"] / (t_idx * 1e-3) / 1e12
         tf_a = alg["attn_flops"] / (t_att * 1e-3) / 1e12
-        tot = (alg["index_flops"] + alg["attn_flops"]) / ((t_idx + t_att) * 1e-3) / 1e12
+        tot = (alg["index_flops"] + alg["attn_flops"]) / (t_all * 1e-3) / 1e12
         schedule = prefill_schedule_of(dp)
         r.update({"bound": "mfma", "algorithmic_TFLOP": (alg["index_flops"] + alg["attn_flops"]) / 1e12,
                   "TFLOP_per_s": tot, "frac_mfma_peak": tot / MFMA_BF16_PEAK_TFLOPS,
@@ -518,15 +548,15 @@ def time_extra(name, steps, warmup):
         device.index_topk(dp, ids)
         device.sparse_attention(dp, ids, out, lse)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = timed_events(steps)
     for e in evs:
         e[0].record()
         device.index_topk(dp, ids)
-        e[1].record()
         device.sparse_attention(dp, ids, out, lse)
         e[2].record()
     torch.cuda.synchronize()
-    r, _ = summarize(inp, dp, ids, evs)
+    split = split_pass(lambda: device.index_topk(dp, ids), lambda: device.sparse_attention(dp, ids, out, lse), steps)
+    r, _ = summarize(inp, dp, ids, evs, split)
     if inp.wl.is_decode:
         r["flushed_reps"] = decode_reps(dp, (ids, out, lse))
         r["flushed_reps"]["GB_per_s_median"] = r["algorithmic_GB"] / (r["flushed_reps"]["ms_median"] * 1e-3)
@@ -591,38 +621,55 @@ def main():
         bufs[name] = (ids, out, lse)
     torch.cuda.synchronize()
 
+    # Markers per step: one at each workload boundary (the end of one workload is the start of the
+    # next), plus one between the index and the attention call of a prefill, whose attention call is
+    # the roofline's kernel and is timed live.  Every marker idles the GPU for a few microseconds, so
+    # a decode carries none between its calls; its split comes from a pass of its own afterwards.
     def step(events=None):
         for i, name in enumerate(names):
             dp = dps[name]
             ids, out, lse = bufs[name]
-            if events is not None:
+            if events is not None and i == 0:
                 events[name][0].record()
             device.index_topk(dp, ids)
-            if events is not None:
+            if events is not None and events[name][1] is not None:
                 events[name][1].record()
             device.sparse_attention(dp, ids, out, lse)
             if events is not None:
                 events[name][2].record()
+
+    def step_events():
+        import torch
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        return {n: [b[i], None if inputs[n].wl.is_decode else torch.cuda.Event(enable_timing=True), b[i + 1]]
+                for i, n in enumerate(names)}
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    ev = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)] for n in names}
+    per_step_ev = [step_events() for _ in range(args.steps)]
+    ev = {n: [e[n] for e in per_step_ev] for n in names}
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step({n: ev[n][s] for n in names})
+    for e in per_step_ev:
+        step(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
     results, kernels = {}, []
     total_tokens = 0
+    split = {}
     for name in names:
-        r, ks = summarize(inputs[name], dps[name], bufs[name][0], ev[name])
+        if inputs[name].wl.is_decode:
+            dp, (ids, out, lse) = dps[name], bufs[name]
+            split[name] = split_pass(lambda: device.index_topk(dp, ids),
+                                     lambda: device.sparse_attention(dp, ids, out, lse), args.steps)
+    for name in names:
+        r, ks = summarize(inputs[name], dps[name], bufs[name][0], ev[name], split.get(name))
         total_tokens += inputs[name].wl.total_q
         results[name] = r
         kernels.extend(ks)

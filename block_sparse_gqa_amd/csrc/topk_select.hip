@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
                                                          const int32_t *__restrict__ cu_k, int num_seqs, int row0,
                                                          int h, int B, int k, int sink, int local,
                                                          int32_t *__restrict__ ids) {
-    __shared__ int hist[kBins];
+    __shared__ __attribute__((aligned(16))) int hist[2][kBins];
     __shared__ int red[2][kNW];
     int nscan = 0;   // scans so far: scan i uses red[i & 1]
     __shared__ uint32_t bc[4];
@@ -158,6 +158,8 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
         for (int x = t; x < k; x += kNT) out[x] = x < E ? x : -1;
         return;
     }
+    // the first pass's histogram starts at zero (the barrier below orders it)
+    for (int i = t; i < kBins / 4; i += kNT) reinterpret_cast<int4 *>(hist[0])[i] = make_int4(0, 0, 0, 0);
     uint32_t key[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -192,20 +194,23 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
         int lo_bit = 32 - __builtin_clz(mx ^ mn);   // bits [0, lo_bit) are undecided
         uint32_t P = mx & ~((lo_bit >= 32) ? 0xffffffffu : ((1u << lo_bit) - 1u));
         int rank = k;   // 1-based rank among keys that match P on the decided bits
-        while (lo_bit > 0) {
+        for (int pass = 0; lo_bit > 0; ++pass) {
             const int w = min(kDigit, lo_bit);
             const int sh = lo_bit - w;
             const uint32_t hi_mask = ~((lo_bit >= 32) ? 0xffffffffu : ((1u << lo_bit) - 1u));
-            for (int b = t; b < (1 << w); b += kNT) hist[b] = 0;
-            __syncthreads();
+            int *hc = hist[pass & 1];
+            // Clear the other histogram for the next pass: its last reads (the
+            // previous pass's scan) came before that pass's decision barrier.
+            for (int i = t; i < kBins / 4; i += kNT)
+                reinterpret_cast<int4 *>(hist[(pass + 1) & 1])[i] = make_int4(0, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < VPT; ++v)
-                if (key[v] != 0u && (key[v] & hi_mask) == P) atomicAdd(&hist[(key[v] >> sh) & ((1u << w) - 1u)], 1);
+                if (key[v] != 0u && (key[v] & hi_mask) == P) atomicAdd(&hc[(key[v] >> sh) & ((1u << w) - 1u)], 1);
             __syncthreads();
             // suffix counts: thread t owns the bins (1<<w)-1-2t and (1<<w)-2-2t (high to low)
             const int nb = 1 << w;
             const int b0 = nb - 1 - 2 * t, b1 = b0 - 1;
-            const int c0 = (b0 >= 0) ? hist[b0] : 0, c1 = (b1 >= 0) ? hist[b1] : 0;
+            const int c0 = (b0 >= 0) ? hc[b0] : 0, c1 = (b1 >= 0) ? hc[b1] : 0;
             int all;
             const int above = block_excl_scan(c0 + c1, red[nscan++ & 1], all);   // keys in bins above b0
             if (b0 >= 0 && above < rank && above + c0 >= rank) {
@@ -246,10 +251,12 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
     // most kNT * 64 = 2^16, so the sum stays below 2^29).
     int both;
     const int ex = block_excl_scan((n_eq << 13) | n_gt, red[nscan++ & 1], both);
+    // Equal keys are kept lowest index first, so the keys kept in lower
+    // threads are their keys > T plus min(their keys == T, need_eq): the
+    // same scan gives every thread its first output place.
     const int need_eq = k - (both & 0x1fff);
     int eq_seen = ex >> 13;
-    int sel = 0;
-    bool take[VPT];
+    int pos = (ex & 0x1fff) + min(eq_seen, need_eq);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         bool tk = key[v] > T;
@@ -257,14 +264,8 @@ __global__ __launch_bounds__(kNT) void topk_select_block(const float *__restrict
             tk = eq_seen < need_eq;
             ++eq_seen;
         }
-        take[v] = tk;
-        sel += tk;
+        if (tk && pos < k) out[pos++] = t * VPT + v;
     }
-    int n_sel;
-    int pos = block_excl_scan(sel, red[nscan++ & 1], n_sel);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v)
-        if (take[v] && pos < k) out[pos++] = t * VPT + v;
 }
 
 template <int VPT>
