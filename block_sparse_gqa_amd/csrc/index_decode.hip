@@ -10,6 +10,7 @@
 // re-laid out through a padded per-wave LDS tile into the MFMA operand
 // layout.  The wave's next two blocks are already in flight in registers while
 // the current one is scored; blocks are dealt round-robin over the waves.
+// Scans larger than the MALL could keep between calls use non-temporal loads.
 //
 // Scores.  Tokens run along the M dimension of v_mfma_f32_16x16x32_bf16 and
 // the h groups along N, so each lane holds 4 tokens of one group per 16-token
@@ -32,8 +33,9 @@ struct IdxTile {
 };
 
 // PAGED: k_idx is a pool of pages of B rows and block j of sequence s sits in
-// page table[s * table_stride + j] (clamped into [0, num_pages)).
-template <int DI, int B, bool PAGED>
+// page table[s * table_stride + j] (clamped into [0, num_pages)).  NT: the
+// index keys are loaded non-temporal.
+template <int DI, int B, bool PAGED, bool NT>
 __global__ __launch_bounds__(256) void index_decode_blockmax(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int h,
@@ -71,10 +73,16 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
         if (ji < E) pages = min(max(table[(size_t)s * table_stride + ji], 0), num_pages - 1);
     }
 
-    // Plain loads (no select on the loaded values, so nothing waits for them
-    // until the block is used); rows past the sequence end repeat its last
-    // key and are masked below.
-    auto load_block = [&](uint4(&r)[T::LOADS], int j) {
+    // Unconditional loads (no select on the loaded values, so nothing waits
+    // for them until the block is used); rows past the sequence end repeat
+    // its last key and are masked below.  A prefetch past the wave's last
+    // block (`real` false) is never scored: plain loads repeat that block, a
+    // cache hit, but a non-temporal load of it would go back to HBM, so those
+    // read the sequence's index-query row instead, which the qop loads above
+    // left in L2.
+    const uint16_t *hot = q_idx + (size_t)row * h * DI;
+    const int hot_elems = h * DI;
+    auto load_block = [&](uint4(&r)[T::LOADS], int j, bool real) {
         j = __builtin_amdgcn_readfirstlane(j);
         const int t0 = j * B;
         // pool row of the block's first token
@@ -90,7 +98,11 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
             const int ci = x * 64 + lane;
             const int tok = ci / T::CPR, c16 = ci % T::CPR;
             const int t = min(tok, len_k - 1 - t0);
-            r[x] = load16(k_idx + (row0 + t) * DI + c16 * 8);
+            const uint16_t *pk = k_idx + (row0 + t) * DI + c16 * 8;
+            if constexpr (NT)
+                r[x] = load16_nt(real ? pk : hot + (ci * 8) % hot_elems);
+            else
+                r[x] = load16(pk);
         }
     };
 
@@ -134,16 +146,16 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
     const int j_last = j_first + (E - 1 - j_first) / nwaves * nwaves;
     uint4 ra[T::LOADS], rb[T::LOADS], rc[T::LOADS];
     int j = j_first;
-    load_block(ra, j);
-    load_block(rb, min(j + nwaves, j_last));
+    load_block(ra, j, true);
+    load_block(rb, min(j + nwaves, j_last), j + nwaves <= j_last);
     for (;; j += 3 * nwaves) {
-        load_block(rc, min(j + 2 * nwaves, j_last));
+        load_block(rc, min(j + 2 * nwaves, j_last), j + 2 * nwaves <= j_last);
         score_block(ra, j);
         if (j + nwaves > j_last) break;
-        load_block(ra, min(j + 3 * nwaves, j_last));
+        load_block(ra, min(j + 3 * nwaves, j_last), j + 3 * nwaves <= j_last);
         score_block(rb, j + nwaves);
         if (j + 2 * nwaves > j_last) break;
-        load_block(rb, min(j + 4 * nwaves, j_last));
+        load_block(rb, min(j + 4 * nwaves, j_last), j + 4 * nwaves <= j_last);
         score_block(rc, j + 2 * nwaves);
         if (j + 3 * nwaves > j_last) break;
     }
@@ -158,12 +170,21 @@ hipError_t launch(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx, 
     const int need = (e_max + kWaves - 1) / kWaves;
     if (per_seq > need) per_seq = need;
     dim3 grid(per_seq, s.num_seqs);
-    if (s.table != nullptr)
-        hipLaunchKernelGGL((index_decode_blockmax<DI, B, true>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q, s.cu_k,
-                           s.h, scores, score_stride(s), s.table, s.table_stride, s.num_pages);
-    else
-        hipLaunchKernelGGL((index_decode_blockmax<DI, B, false>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q,
-                           s.cu_k, s.h, scores, score_stride(s), nullptr, 0, 0);
+    // 4 x 1M context (537 MB of index keys): 109 -> 105 us of index_topk with
+    // non-temporal loads; 8 x 64K (67 MB) stays plain: 24 us back to back,
+    // against 29 us non-temporal, since plain loads leave it in the MALL.
+    const bool nt = (double)s.total_k * DI * 2.0 > kDecodeStreamBytes;
+    auto go = [&](auto paged, auto ntag) {
+        constexpr bool P = decltype(paged)::value, N = decltype(ntag)::value;
+        hipLaunchKernelGGL((index_decode_blockmax<DI, B, P, N>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q, s.cu_k,
+                           s.h, scores, score_stride(s), P ? s.table : nullptr, P ? s.table_stride : 0,
+                           P ? s.num_pages : 0);
+    };
+    if (s.table != nullptr) {
+        if (nt) go(std::true_type{}, std::true_type{}); else go(std::true_type{}, std::false_type{});
+    } else {
+        if (nt) go(std::false_type{}, std::true_type{}); else go(std::false_type{}, std::false_type{});
+    }
     return hipGetLastError();
 }
 

@@ -46,6 +46,12 @@ inline int score_stride(const Shape &s) {
     return (e + 3) / 4 * 4;
 }
 
+// Bytes a decode call streams (the index keys it scans, or the K/V it
+// selects) above which its loads are non-temporal: more than the 256 MB MALL
+// could keep for the next call, where plain loads let consecutive calls find
+// smaller inputs there.
+constexpr double kDecodeStreamBytes = 192.0 * (1 << 20);
+
 // Index branch, step 1+2: token scores (never stored) max-pooled per block.
 hipError_t launch_index_prefill(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx,
                                 float *scores, hipStream_t st);

@@ -365,7 +365,6 @@ __global__ __launch_bounds__(64) void attn_decode_merge(const float *__restrict_
         lse[(size_t)s * H + head] = wsum > 0.f ? (m + log2f(wsum)) * 0.69314718055994531f : -INFINITY;
 }
 
-constexpr double kDecodeStreamBytes = 192.0 * (1 << 20);   // selected K/V per call above which loads are nt
 
 // K and V bytes a decode call gathers: top_k blocks of each per (sequence, group).
 double decode_selected_bytes(const Shape &s) { return (double)s.num_seqs * s.h * s.top_k * s.B * s.d * 2.0 * 2.0; }
