@@ -163,13 +163,14 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
 
 template <int DI, int B>
 hipError_t launch(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx, float *scores, hipStream_t st) {
-    // about 4096 workgroups in all, each wave taking every nwaves-th block
-    // (1M context: 109 us against 111 us with 2048 and 114 us with 1024 or
-    // 8192).  A paged cache takes 2048: each wave first reads its blocks'
-    // pages, a dependent load that longer-lived waves pay less often (paged
-    // 4 x 1M decode 0.282 -> 0.276 ms; 1024: 0.278 ms).
+    // About 1536 workgroups in all, each wave taking every nwaves-th block:
+    // two rounds of the 768 that fit at once (three per CU, by registers), so
+    // no round runs on part of the chip.  4 x 1M context, index_topk: 103.5 us
+    // against 107-108.5 with 768, 3072 and 4096; the paged form ties with
+    // 2048 and beats 4096 (its waves first read their blocks' pages, a
+    // dependent load that longer-lived waves pay less often).
     const int e_max = (s.max_k + s.B - 1) / s.B;
-    int per_seq = ((s.table != nullptr ? 2048 : 4096) + s.num_seqs - 1) / s.num_seqs;
+    int per_seq = (1536 + s.num_seqs - 1) / s.num_seqs;
     const int need = (e_max + kWaves - 1) / kWaves;
     if (per_seq > need) per_seq = need;
     dim3 grid(per_seq, s.num_seqs);
