@@ -726,6 +726,14 @@ def main():
     ce[1].record()
     torch.cuda.synchronize()
     copy_gbs = 2 * (1 << 32) * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    # a write-only stream: torch's fill of the same 4 GiB
+    dst.fill_(1)
+    ce[0].record()
+    for _ in range(5):
+        dst.fill_(1)
+    ce[1].record()
+    torch.cuda.synchronize()
+    write_gbs = (1 << 32) * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
     del dst
     # a read-only stream of the same 4 GiB and a pure MFMA loop, from the library's own kernels
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -780,10 +788,11 @@ def main():
         "results": results,
         "roofline": roofline,
         "ceilings": {"hbm_copy_GB_per_s": copy_gbs, "hbm_stream_read_GB_per_s": read_gbs,
+                     "hbm_fill_GB_per_s": write_gbs,
                      "mfma_bf16_TFLOP_per_s": mfma_tfs,
                      "note": "measured on this GPU: a device-to-device copy of 4 GiB (read + write bytes), a "
-                             "full-line non-temporal read-only stream of the same 4 GiB, and back-to-back 16x16x32 "
-                             "bf16 MFMAs with no memory traffic"},
+                             "fill of the same 4 GiB (write bytes), a full-line non-temporal read-only stream of "
+                             "them, and back-to-back 16x16x32 bf16 MFMAs with no memory traffic"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
