@@ -163,21 +163,24 @@ __global__ __launch_bounds__(256) void index_decode_blockmax(
 
 template <int DI, int B>
 hipError_t launch(const Shape &s, const uint16_t *q_idx, const uint16_t *k_idx, float *scores, hipStream_t st) {
-    // About 1536 workgroups in all, each wave taking every nwaves-th block:
-    // two rounds of the 768 that fit at once (three per CU, by registers), so
-    // no round runs on part of the chip.  4 x 1M context, index_topk: 103.5 us
-    // against 107-108.5 with 768, 3072 and 4096; the paged form ties with
-    // 2048 and beats 4096 (its waves first read their blocks' pages, a
-    // dependent load that longer-lived waves pay less often).
-    const int e_max = (s.max_k + s.B - 1) / s.B;
-    int per_seq = (1536 + s.num_seqs - 1) / s.num_seqs;
-    const int need = (e_max + kWaves - 1) / kWaves;
-    if (per_seq > need) per_seq = need;
-    dim3 grid(per_seq, s.num_seqs);
     // 4 x 1M context (537 MB of index keys): 109 -> 105 us of index_topk with
     // non-temporal loads; 8 x 64K (67 MB) stays plain: 24 us back to back,
     // against 29 us non-temporal, since plain loads leave it in the MALL.
     const bool nt = (double)s.total_k * DI * 2.0 > kDecodeStreamBytes;
+    // Each wave takes every nwaves-th block.  A streamed scan runs on about
+    // 1536 workgroups: two rounds of the 768 that fit at once (three per CU,
+    // by registers), so no round runs on part of the chip.  4 x 1M context,
+    // index_topk: 103.5 us against 107-108.5 with 768, 3072 and 4096; the
+    // paged form ties with 2048 and beats 4096 (its waves first read their
+    // blocks' pages, a dependent load that longer-lived waves pay less often).
+    // A scan the MALL holds takes one round of 768: 8 x 64K decode 52.8 us
+    // against 53.7 us with 1536 back to back (57.8 against 60.0 behind a
+    // flush).
+    const int e_max = (s.max_k + s.B - 1) / s.B;
+    int per_seq = ((nt ? 1536 : 768) + s.num_seqs - 1) / s.num_seqs;
+    const int need = (e_max + kWaves - 1) / kWaves;
+    if (per_seq > need) per_seq = need;
+    dim3 grid(per_seq, s.num_seqs);
     auto go = [&](auto paged, auto ntag) {
         constexpr bool P = decltype(paged)::value, N = decltype(ntag)::value;
         hipLaunchKernelGGL((index_decode_blockmax<DI, B, P, N>), grid, dim3(256), 0, st, q_idx, k_idx, s.cu_q, s.cu_k,
