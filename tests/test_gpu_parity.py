@@ -296,6 +296,10 @@ LONG = [
     ("decode_e62k", (1,), (4_000_000,), 2, 1, 64, 32, 64, 64),
     # 1250 blocks: one wave per row with 32 keys per lane
     ("prefill_e1250", (80_000,), (80_000,), 4, 2, 64, 32, 64, 8),
+    # index keys above the 192 MiB line (non-temporal scan) with short sequences beside the long one: their waves
+    # score at most one block, so every prefetch past it reads the L2-resident query row; one cache is a single
+    # partial block
+    ("decode_mixed_streamed", (1, 1, 1, 1), (3_300_000, 100, 5000, 40), 4, 2, 64, 32, 64, 16),
 ]
 
 
