@@ -444,6 +444,29 @@ def prefill_schedules(dp, bufs, fwd, steps):
     return res
 
 
+def forced_index(dp, ids, steps, sink=1, local=1):
+    """The index branch with forced blocks (msa_index_topk_ex: the first `sink` and the last `local` eligible
+    blocks of every row always kept), timed against the plain msa_index_topk in the same way, back to back on
+    the same inputs.  Reported beside the headline."""
+    import torch
+
+    from block_sparse_gqa_amd import device
+    fids = device.index_topk_forced(dp, sink, local)   # warm-up
+    res = {"sink_blocks": sink, "local_blocks": local}
+    for key, call in (("plain_ms", lambda: device.index_topk(dp, ids)),
+                      ("forced_ms", lambda: device.index_topk_forced(dp, sink, local, fids))):
+        call()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(steps):
+            call()
+        e[1].record()
+        torch.cuda.synchronize()
+        res[key] = e[0].elapsed_time(e[1]) / steps
+    del fids
+    return res
+
+
 def prefill_schedule_of(dp):
     """What msa_sparse_attn_prefill runs for this problem, read from its workspace size: the query tiles,
     the block-centric schedule, or both (tiles for the early rows, the block-centric schedule after)."""
@@ -578,6 +601,8 @@ def main():
                     help="skip the sparse-branch backward measurement (reported beside the headline, not in it)")
     ap.add_argument("--no-schedules", action="store_true",
                     help="skip timing both prefill schedules explicitly (reported beside the headline)")
+    ap.add_argument("--no-forced", action="store_true",
+                    help="skip timing the index branch with forced sink/local blocks (reported beside the headline)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement (reported beside the headline, not in it)")
     ap.add_argument("--no-extra", action="store_true",
@@ -700,6 +725,10 @@ def main():
             if not inputs[name].wl.is_decode:
                 results[name]["schedules"] = prefill_schedules(dps[name], bufs[name], results[name],
                                                                max(args.steps // 2, 3))
+
+    if not args.no_forced:
+        for name in names:
+            results[name]["forced"] = forced_index(dps[name], bufs[name][0], max(args.steps // 2, 3))
 
     if not args.no_paged:
         for name in names:
